@@ -1,0 +1,229 @@
+/*
+ * vegas_attn.h -- C-ABI of the MI355X (gfx950) hot path of Vegas's
+ * verification-guided sparse attention, one decode iteration of one layer:
+ *
+ *   vg_verify_attention        full causal attention of the gamma+1 verify
+ *                              rows over the whole paged KV cache, exporting
+ *                              the pre-softmax logits of row 0 (first draft
+ *                              token) and row gamma (bonus token).
+ *   vg_aggregate_scores        one score per prefix position: the exported
+ *                              logits summed over rows and query heads.
+ *   vg_topk_select             the k prefix positions with the largest
+ *                              scores, as ascending positions and as
+ *                              page-size-1 slot ids.
+ *   vg_sparse_draft_attention  attention of draft rows over only the selected
+ *                              slots plus the causal tail after the prefix.
+ *
+ * "Vegas" below is the page "Vegas: Self-Speculative Decoding with
+ * Verification-Guided Sparse Attention" (technical summary).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every tensor pointer is DEVICE memory owned by the caller.  The library
+ *   allocates nothing, keeps no per-call state between calls except inside
+ *   the caller's workspace, and never synchronises the stream or copies
+ *   device data to the host.  Work is enqueued on `stream` (a hipStream_t
+ *   passed as void*; NULL = the null stream).
+ * - Arguments are validated on the host before anything is enqueued.  On any
+ *   error nothing is launched and no output is touched.  Values that live on
+ *   the device (prefix lengths, k, page-table entries, slot ids) cannot be
+ *   checked without a synchronisation; their preconditions are stated per
+ *   call, and violating them is undefined behaviour.
+ * - Device pointers must be 16-byte aligned.
+ * - Workspaces: sized by the matching *_workspace_size query, and zero-filled
+ *   once before first use (vg_workspace_zero does it).  Every call leaves its
+ *   workspace zero-filled again where it needs zeros, so a workspace can be
+ *   reused by later calls on the same stream; it must not be shared by calls
+ *   that may run concurrently.
+ * - KV cache layout: token-major paged cache, element [slot][kv_head][d] with
+ *   slot = page * page_size + offset, i.e. [num_pages][page_size][Hkv][D].
+ *   A slot id is the index of a page of one token (Vegas section 3, sparse
+ *   execution: selected token indices are passed as page indices of a
+ *   page-size-1 PagedAttention call).
+ * - Query head h uses KV head h / (Hq / Hkv).
+ * - Outputs are fp32.
+ */
+#ifndef VEGAS_ATTN_H
+#define VEGAS_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t vg_status;
+#define VG_OK 0
+#define VG_ERR_INVALID_ARG 1  /* a null/misaligned pointer or an out-of-range argument */
+#define VG_ERR_UNSUPPORTED 2  /* a valid shape this build has no kernel for */
+#define VG_ERR_WORKSPACE 3    /* workspace missing or smaller than the size query says */
+#define VG_ERR_HIP 4          /* the HIP runtime rejected a launch */
+
+#define VG_DTYPE_F32 0
+#define VG_DTYPE_BF16 1
+
+#define VG_KERNEL_AUTO 0 /* MFMA for bf16, VALU for f32 */
+#define VG_KERNEL_VALU 1 /* vector-ALU contraction (f32 and bf16) */
+#define VG_KERNEL_MFMA 2 /* matrix-core contraction (bf16 only) */
+
+/* Shape of one attention layer and its paged cache. */
+typedef struct vg_shape {
+  int32_t batch;             /* B >= 1 sequences */
+  int32_t num_q_heads;       /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;      /* Hkv >= 1 */
+  int32_t head_dim;          /* D: 64 or 128 */
+  int32_t page_size;         /* tokens per page: 16 */
+  int32_t max_pages_per_seq; /* row length of page_table */
+  int32_t dtype;             /* VG_DTYPE_*: element type of q, k_cache, v_cache */
+  float softmax_scale;       /* logit = softmax_scale * q.k; <= 0 selects 1/sqrt(D) */
+  int32_t kernel;            /* VG_KERNEL_* */
+} vg_shape;
+
+/* Human-readable name of a status code (static string). */
+const char *vg_status_string(vg_status status);
+
+/* Library version string (static). */
+const char *vg_version(void);
+
+/* Zero-fill `bytes` of device workspace on `stream` (a kernel, no memset node). */
+vg_status vg_workspace_zero(void *workspace, size_t bytes, void *stream);
+
+/* ---------------------------------------------------------------- verify */
+
+/* Workspace bytes vg_verify_attention needs for this shape and these maxima. */
+vg_status vg_verify_workspace_size(const vg_shape *shape, int32_t max_prefix, int32_t gamma,
+                                   size_t *bytes);
+
+/*
+ * Verification attention with the Collect-2-Query logit export.
+ *
+ * Vegas section 2 (core mechanism, verification phase): verification is a
+ * standard full-attention pass that computes the attention logits of every KV
+ * entry.  Section 2.B (Collect-2-Query): only the first draft token and the
+ * bonus token export their logits.  Section 3 (kernel instrumentation): the
+ * logits are written to HBM before softmax normalisation.
+ *
+ * For each sequence b with prefix length P_b = prefix_len[b], the cache holds
+ * N_b = P_b + gamma + 1 tokens at logical positions 0..N_b-1 (the gamma+1 new
+ * tokens already appended at P_b..P_b+gamma).  Row r in [0, gamma] attends
+ * causally to positions 0..P_b+r:
+ *     l[r][h][j] = scale * q[b][r][h] . K[b][j][h/G]
+ *     out[b][r][h] = sum_j softmax_j(l[r][h][.]) V[b][j][h/G]
+ *
+ *   q            [B][gamma+1][Hq][D]  dtype
+ *   k_cache      [num_slots][Hkv][D]  dtype
+ *   v_cache      [num_slots][Hkv][D]  dtype
+ *   page_table   [B][max_pages_per_seq] int32: logical page -> physical page
+ *   prefix_len   [B] int32, 0 <= P_b <= max_prefix, and
+ *                ceil((P_b+gamma+1)/page_size) <= max_pages_per_seq
+ *   gamma        0 <= gamma <= 15 (draft tokens; gamma+1 verify rows)
+ *   out          [B][gamma+1][Hq][D] float (written)
+ *   logits       [B][2][Hq][max_prefix] float, nullable: [b][0][h][j] = l[0][h][j],
+ *                [b][1][h][j] = l[gamma][h][j] for j < P_b (natural-log units,
+ *                scale applied); entries j >= P_b are not written.
+ *   group_scores [B][Hkv][max_prefix] float, nullable: sum over the G query
+ *                heads of KV head g of both exported rows, for j < P_b.
+ *   At least one of logits / group_scores must be non-null.
+ * Supported: D in {64, 128}; page_size 16; (gamma+1)*G <= 64; bf16 with any
+ * kernel, f32 with VG_KERNEL_VALU or AUTO.
+ */
+vg_status vg_verify_attention(const vg_shape *shape, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *page_table,
+                              const int32_t *prefix_len, int32_t max_prefix, int32_t gamma,
+                              float *out, float *logits, float *group_scores, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------- aggregate */
+
+/*
+ * Score of each prefix position (Vegas section 2.A, selection objective,
+ * restricted by section 2.B to the exported rows):
+ *     scores[b][j] = sum_{t < src_rows} sum_{h < src_heads} src[b][t][h][j],  j < P_b.
+ * Use src = logits with (src_rows, src_heads) = (2, Hq), or src = group_scores
+ * with (1, Hkv).  Entries j >= P_b of `scores` are not written.
+ *
+ *   src         [B][src_rows][src_heads][max_prefix] float
+ *   prefix_len  [B] int32, 0 <= P_b <= max_prefix
+ *   scores      [B][max_prefix] float (written)
+ *   select_ws   nullable.  A vg_topk_select workspace sized for (batch,
+ *               max_prefix).  When given, the first pass of the top-k
+ *               selection over the new scores is fused into this call and its
+ *               result kept in select_ws; pass VG_TOPK_PREPASS_DONE to the next
+ *               vg_topk_select on the same scores and workspace.
+ */
+vg_status vg_aggregate_scores(int32_t batch, const float *src, int32_t src_rows, int32_t src_heads,
+                              const int32_t *prefix_len, int32_t max_prefix, float *scores,
+                              void *select_ws, size_t select_ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ topk */
+
+#define VG_TOPK_PREPASS_DONE 1 /* vg_aggregate_scores already ran the first pass */
+
+/* Workspace bytes vg_topk_select (and a fused vg_aggregate_scores) needs. */
+vg_status vg_topk_workspace_size(int32_t batch, int32_t max_prefix, size_t *bytes);
+
+/*
+ * Exact top-k selection (Vegas section 2.A: T maximises the summed score over
+ * all subsets of k prefix positions; the sum is additive over positions, so T
+ * is the set of the k largest scores).
+ *
+ * For each b, with kk = min(k[b], P_b): writes the kk positions j < P_b with
+ * the largest scores[b][j], ascending, to sel_pos[b][0..kk); equal scores at
+ * the threshold are taken lowest position first (-0.0 counts as +0.0);
+ * sel_count[b] = kk.  sel_slot (nullable) receives the page-size-1 slot of
+ * each position: page_table[b][pos / page_size] * page_size + pos % page_size.
+ * Entries past kk are not written.  Scores must be finite.
+ *
+ *   scores      [B][max_prefix] float
+ *   prefix_len  [B] int32, 0 <= P_b <= max_prefix
+ *   k           [B] int32, 0 <= k[b] <= max_k
+ *   page_table  [B][max_pages_per_seq] int32 (needed when sel_slot is non-null)
+ *   sel_pos     [B][max_k] int32;  sel_slot [B][max_k] int32;  sel_count [B] int32
+ *   flags       0 or VG_TOPK_PREPASS_DONE
+ */
+vg_status vg_topk_select(int32_t batch, const float *scores, int32_t max_prefix,
+                         const int32_t *prefix_len, const int32_t *k, int32_t max_k,
+                         const int32_t *page_table, int32_t page_size, int32_t max_pages_per_seq,
+                         int32_t *sel_pos, int32_t *sel_slot, int32_t *sel_count, int32_t flags,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* --------------------------------------------------------- sparse draft */
+
+/* Workspace bytes vg_sparse_draft_attention needs. */
+vg_status vg_sparse_draft_workspace_size(const vg_shape *shape, int32_t n_q, int32_t max_k,
+                                         int32_t max_tail, size_t *bytes);
+
+/*
+ * Sparse draft attention (Vegas section 2, core mechanism, drafting phase:
+ * attention restricted to the selected critical entries; section 3, sparse
+ * execution: the selected token indices are the pages of a page-size-1
+ * PagedAttention call).
+ *
+ * Row i in [0, n_q) of sequence b attends to the key list
+ *     sel_slot[b][0..cnt)  ++  slots of positions tail_start[b] .. tail_start[b]+tail_len[b]-n_q+i
+ * (cnt = sel_count[b]; tail positions translated through page_table):
+ *     out[b][i][h] = sum over the list of softmax(scale * q.K) V  (KV head h/G).
+ *
+ *   q          [B][n_q][Hq][D] dtype, 1 <= n_q and n_q * G <= 64
+ *   sel_slot   [B][max_k] int32 slot ids (as written by vg_topk_select)
+ *   sel_count  [B] int32, 0 <= cnt <= max_k
+ *   page_table [B][max_pages_per_seq] int32
+ *   tail_start [B] int32 >= 0;  tail_len [B] int32 with n_q <= tail_len <= max_tail,
+ *              every tail position within the sequence's pages
+ *   max_tail   host-side bound on tail_len, n_q <= max_tail
+ *   out        [B][n_q][Hq][D] float (written)
+ */
+vg_status vg_sparse_draft_attention(const vg_shape *shape, const void *q, int32_t n_q,
+                                    const void *k_cache, const void *v_cache,
+                                    const int32_t *sel_slot, const int32_t *sel_count,
+                                    int32_t max_k, const int32_t *page_table,
+                                    const int32_t *tail_start, const int32_t *tail_len,
+                                    int32_t max_tail, float *out, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VEGAS_ATTN_H */

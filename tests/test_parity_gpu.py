@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path (through the C-ABI) against the fp64 oracle.
+
+Each step is checked in isolation on the oracle's own inputs (fp32-rounded
+where the GPU step consumes fp32), then the chain end to end.  Gates are the
+contract tolerances of tests/parity.py; integer outputs are bit-exact.
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import parity
+from verification_guided_sparse_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = min(16, os.cpu_count() or 1)
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available()
+    from verification_guided_sparse_amd import _binding
+    _binding.lib()  # fail loudly if the HIP library is missing
+    return torch
+
+
+def _oracle_all(c):
+    out, logits, group, _ = oracle.verify(c.q, c.k_cache, c.v_cache, c.page_table, c.prefix_len,
+                                          c.gamma, c.scale, nthreads=NTHREADS)
+    return out, logits, group
+
+
+def _rows_mask(c, lead):
+    return parity.prefix_mask(c.prefix_len, c.max_prefix, lead)
+
+
+def _check(ok_msg, what):
+    ok, msg = ok_msg
+    assert ok, f"{what}: {msg}"
+
+
+def _run_steps(c, kernel=None):
+    """Per-step parity of one case; returns the device case for further checks."""
+    from verification_guided_sparse_amd import _binding as vg
+    from verification_guided_sparse_amd.runner import DeviceCase
+    import torch
+    _say(f"[parity] {c.cfg.name} B={c.batch} P={list(c.prefix_len)} Hq={c.num_q_heads} "
+         f"Hkv={c.num_kv_heads} D={c.head_dim} {c.dtype} gamma={c.gamma} kernel={kernel}")
+    dc = DeviceCase(c, kernel=vg.VG_KERNEL_AUTO if kernel is None else kernel)
+    out_ref, logits_ref, group_ref = _oracle_all(c)
+
+    # verify + export (both forms)
+    dc.verify(export="both")
+    torch.cuda.synchronize()
+    _check(parity.output_gate(dc.host("out"), out_ref), "verify out")
+    _check(parity.score_gate(dc.host("logits"), logits_ref, mask=_rows_mask(c, (2, c.num_q_heads))),
+           "verify logits")
+    _check(parity.score_gate(dc.host("group"), group_ref, mask=_rows_mask(c, (c.num_kv_heads,))),
+           "verify group scores")
+
+    # aggregate on the oracle's logits (fp32-rounded), both sources
+    lg32 = torch.from_numpy(logits_ref.astype(np.float32)).cuda()
+    gr32 = torch.from_numpy(group_ref.astype(np.float32)).cuda()
+    dc.logits.copy_(lg32)
+    dc.group.copy_(gr32)
+    mask_s = _rows_mask(c, ())
+    for src, ref_src in (("raw", logits_ref.astype(np.float32)), ("group", group_ref.astype(np.float32))):
+        dc.aggregate(src=src)
+        torch.cuda.synchronize()
+        s_ref = oracle.aggregate(ref_src.astype(np.float64), c.prefix_len)
+        _check(parity.score_gate(dc.host("scores"), s_ref, mask=mask_s), f"aggregate {src}")
+
+    # top-k on the oracle's scores rounded to fp32: bit-exact against the oracle
+    # taking the same decision in the same precision
+    s_ref = oracle.aggregate(logits_ref, c.prefix_len)
+    s32 = s_ref.astype(np.float32)
+    dc.scores.copy_(torch.from_numpy(s32).cuda())
+    dc.topk()
+    torch.cuda.synchronize()
+    pos_ref, slot_ref, cnt_ref = oracle.topk(s32.astype(np.float64), c.prefix_len, c.k,
+                                             page_table=c.page_table, max_k=dc.max_k)
+    cnt = dc.host("sel_count")
+    _check(parity.exact_gate(cnt, cnt_ref), "topk count")
+    pos, slot = dc.host("sel_pos"), dc.host("sel_slot")
+    for b in range(c.batch):
+        n = int(cnt_ref[b])
+        _check(parity.exact_gate(pos[b, :n], pos_ref[b, :n]), f"topk positions seq {b}")
+        _check(parity.exact_gate(slot[b, :n], slot_ref[b, :n]), f"topk slots seq {b}")
+
+    # sparse draft on the oracle's selection, every draft step's tail
+    for s in range(c.gamma):
+        dc.sel_slot.copy_(torch.from_numpy(slot_ref).cuda())
+        dc.sel_count.copy_(torch.from_numpy(cnt_ref).cuda())
+        dc.sparse(step=s)
+        torch.cuda.synchronize()
+        o_ref = oracle.sparse(np.ascontiguousarray(c.q_draft[s][:, None]), c.k_cache, c.v_cache,
+                              c.page_table, pos_ref, cnt_ref, c.prefix_len,
+                              np.full(c.batch, s + 1, np.int32), c.scale, nthreads=NTHREADS)
+        _check(parity.output_gate(dc.host("draft_out"), o_ref), f"sparse draft step {s}")
+    return dc, (out_ref, logits_ref, group_ref, s_ref)
+
+
+def _run_chain(c, dc, refs, export):
+    """End to end on the GPU's own intermediate results."""
+    import torch
+    out_ref, logits_ref, group_ref, s_ref = refs
+    dc.iteration(export=export)
+    torch.cuda.synchronize()
+    _check(parity.output_gate(dc.host("out"), out_ref), f"chain[{export}] verify out")
+    _check(parity.score_gate(dc.host("scores"), s_ref, mask=_rows_mask(c, ())), f"chain[{export}] scores")
+    pos, cnt = dc.host("sel_pos"), dc.host("sel_count")
+    _check(parity.topk_gate(pos, cnt, s_ref, c.prefix_len, c.k), f"chain[{export}] topk")
+    slot = dc.host("sel_slot")
+    for b in range(c.batch):
+        n = int(cnt[b])
+        p = pos[b, :n].astype(np.int64)
+        expect = c.page_table[b, p // c.page_size].astype(np.int64) * c.page_size + p % c.page_size
+        _check(parity.exact_gate(slot[b, :n], expect), f"chain[{export}] slot translation seq {b}")
+    # last draft step, against the oracle over the GPU's own selection
+    s = c.gamma - 1
+    o_ref = oracle.sparse(np.ascontiguousarray(c.q_draft[s][:, None]), c.k_cache, c.v_cache,
+                          c.page_table, pos, cnt, c.prefix_len, np.full(c.batch, s + 1, np.int32),
+                          c.scale, nthreads=NTHREADS)
+    _check(parity.output_gate(dc.host("draft_out"), o_ref), f"chain[{export}] sparse draft")
+
+
+# ------------------------------------------------------------------ small cases
+
+SMALL = {
+    "c1_tiny": lambda: synth.CONFIGS["c1_tiny"],
+    "c1_tiny_sharp": lambda: synth.sharp(synth.CONFIGS["c1_tiny"]),
+    "c2_small": lambda: synth.small("c2_qwen3_32k", prefix=(3001,)),
+    "c2_small_sharp": lambda: synth.sharp(synth.small("c2_qwen3_32k", prefix=(3001,))),
+    "c3_small": lambda: synth.small("c3_qwen3_128k", prefix=(9000,), span_len=64),
+    "c4_small": lambda: synth.small("c4_ragged_b8", prefix=(700, 1531, 4097)),
+    "c5_small": lambda: synth.small("c5_gptoss_64k", prefix=(2000, 2077)),
+    "c5_small_sharp": lambda: synth.sharp(synth.small("c5_gptoss_64k", prefix=(2000, 2077))),
+    "short_prefixes": lambda: synth.small("c2_qwen3_32k", prefix=(1, 5, 17, 33), gamma=4, k_pct=50),
+    "short_prefixes_g8": lambda: synth.small("c5_gptoss_64k", prefix=(3, 16, 31, 64), gamma=5, k_pct=50),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_parity(torch_cuda, name):
+    c = synth.make_case(SMALL[name]())
+    dc, refs = _run_steps(c)
+    _run_chain(c, dc, refs, "group")
+    _run_chain(c, dc, refs, "raw")
+
+
+@pytest.mark.parametrize("name", ["c2_small", "c5_small", "short_prefixes"])
+def test_small_parity_valu_bf16(torch_cuda, name):
+    from verification_guided_sparse_amd import _binding as vg
+    c = synth.make_case(SMALL[name]())
+    _run_steps(c, kernel=vg.VG_KERNEL_VALU)
+
+
+def test_page_permutation_bit_identical(torch_cuda):
+    """Same logical data under identity and permuted page tables: identical bits."""
+    import torch
+    from verification_guided_sparse_amd.runner import DeviceCase
+    cfg = synth.small("c2_qwen3_32k", prefix=(2500, 1200))
+    res = []
+    for paging in ("identity", "permuted"):
+        c = synth.make_case(synth.dataclasses.replace(cfg, paging=paging))
+        dc = DeviceCase(c)
+        dc.iteration(export="both")
+        torch.cuda.synchronize()
+        res.append((dc.host("out"), dc.host("logits"), dc.host("group"), dc.host("scores"),
+                    dc.host("sel_pos"), dc.host("draft_out")))
+    for a, b in zip(*res):
+        assert np.array_equal(a, b)
+
+
+def test_bit_reproducible(torch_cuda):
+    import torch
+    from verification_guided_sparse_amd.runner import DeviceCase
+    c = synth.make_case(synth.small("c5_gptoss_64k", prefix=(3000, 4100)))
+    dc = DeviceCase(c)
+    outs = []
+    for _ in range(2):
+        dc.iteration(export="raw")
+        torch.cuda.synchronize()
+        outs.append([dc.host(n).copy() for n in ("out", "logits", "scores", "sel_pos", "sel_slot", "draft_out")])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
+def test_topk_ties_and_edges(torch_cuda):
+    """Integer-valued scores with many ties, k = 0, k > P, P = 0 and -0.0 vs +0.0."""
+    import torch
+    from verification_guided_sparse_amd import _binding as vg
+    B, mp = 6, 5000
+    rng = np.random.default_rng(11)
+    s = rng.integers(-3, 4, size=(B, mp)).astype(np.float32)
+    s[3, ::2] = -0.0
+    s[3, 1::2] = 0.0
+    P = np.array([5000, 4097, 0, 3000, 2048, 1], np.int32)
+    k = np.array([2500, 0, 7, 1500, 2048, 5], np.int32)
+    max_k = 2500
+    pt = np.arange(B * 320, dtype=np.int32).reshape(B, 320)
+    dev = dict(device="cuda")
+    ts = torch.from_numpy(s).cuda()
+    tP, tk, tpt = (torch.from_numpy(x).cuda() for x in (P, k, pt))
+    pos = torch.full((B, max_k), -1, dtype=torch.int32, **dev)
+    slot = torch.full((B, max_k), -1, dtype=torch.int32, **dev)
+    cnt = torch.zeros(B, dtype=torch.int32, **dev)
+    nbytes = vg.vg_topk_workspace_size(B, mp)
+    ws = torch.empty(nbytes, dtype=torch.uint8, **dev)
+    vg.vg_workspace_zero(ws, nbytes)
+    for rep in range(2):  # the workspace must come back clean
+        vg.vg_topk_select(B, ts, mp, tP, tk, max_k, tpt, 16, 320, pos, slot, cnt, 0, ws, nbytes)
+        torch.cuda.synchronize()
+        pr, sr, cr = oracle.topk(s.astype(np.float64), P, k, page_table=pt, max_k=max_k)
+        assert np.array_equal(cnt.cpu().numpy(), cr)
+        hp, hs = pos.cpu().numpy(), slot.cpu().numpy()
+        for b in range(B):
+            n = int(cr[b])
+            assert np.array_equal(hp[b, :n], pr[b, :n]), (rep, b)
+            assert np.array_equal(hs[b, :n], sr[b, :n]), (rep, b)
+
+
+# ------------------------------------------------------------------ full sizes
+
+@pytest.mark.parametrize("name", ["c1_tiny", "c2_qwen3_32k", "c3_qwen3_128k", "c5_gptoss_64k", "c4_ragged_b8"])
+def test_full_size_parity(torch_cuda, name):
+    """Every workload at its full size, in the launch configuration the benchmark times."""
+    c = synth.make_case(name)
+    dc, refs = _run_steps(c)
+    _run_chain(c, dc, refs, "group")

@@ -1,0 +1,299 @@
+// attn_mfma.h -- bf16 split-KV attention on the CDNA4 matrix cores
+// (v_mfma_f32_16x16x32_bf16), used for both verification attention (all
+// cache positions, causal among the new rows, logit export) and sparse draft
+// attention (selected slots + causal tail).
+//
+// One workgroup = 4 waves = one (split, KV head g, sequence b).  The query
+// rows of KV head g (M = nrows * G, padded to NT tiles of 16) stay in
+// registers for the whole split.  Each wave walks 32-entry tiles of the
+// split's key list (tiles t = wave, wave + 4, ...):
+//
+//   S^T[tok][row] = K[tok][:] . Q[row][:]     A = K rows straight from HBM,
+//                                             B = Q^T held in registers
+//   online softmax over tok, per row          (log2 domain, fp32)
+//   O^T[d][row] += V^T[d][tok] P^T[tok][row]  A = V^T built in registers from
+//                                             full-row V loads, B = P^T (bf16)
+//
+// Lane l = 16*q4 + i16.  MFMA 16x16x32 operands: lane holds A[i16][8*q4 .. +7]
+// and B[8*q4 .. +7][i16]; the result C[4*q4 + c][i16], c = 0..3.
+//  * K: lane loads 16 bytes of token (tt*16 + i16), d-chunk 4*ks + q4.  The
+//    contraction over d may visit d in any order as long as Q uses the same
+//    one, so the four q4 lanes of a token read 64 contiguous bytes.
+//  * V: lane loads d-chunk i16 of the 8 tokens tok(q4, v); 16 lanes cover one
+//    full 256-byte (D = 128) or 128-byte (D = 64) row per instruction.  Their
+//    8 x 8 (or 8 x 4) bf16 are repacked with byte permutes so that MFMA tile
+//    `at` holds d = DPL*i16 + at for the 8 tokens.
+//  * tok(q4, v) = v < 4 ? 4*q4 + v : 16 + 4*q4 + (v - 4) is exactly the token
+//    set lane (q4, i16) holds in the S^T result, so P^T needs no lane movement.
+#pragma once
+
+#include "attn_common.h"
+
+namespace vg {
+
+template <int D>
+struct VRow;  // one lane's slice of one V row
+template <>
+struct VRow<128> {
+  u32x4 w;  // d = 8*i16 .. 8*i16 + 7
+};
+template <>
+struct VRow<64> {
+  u32x2 w;  // d = 4*i16 .. 4*i16 + 3
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint32_t pack_lo(uint32_t x, uint32_t y) {
+  return (x & 0xffffu) | (y << 16);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t x, uint32_t y) {
+  return (x >> 16) | (y & 0xffff0000u);
+}
+
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+template <int D, int NT, bool FUSED>
+__global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, uint32_t *counters) {
+  constexpr int KS = D / 32;   // k-steps of the QK^T contraction
+  constexpr int DPL = D / 16;  // d values per lane per V row, = number of PV tiles
+  constexpr int ROWS = NT * 16;
+  __shared__ MergeSmem<ROWS, D> sm;
+  __shared__ int sm_flag;
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q4 = lane >> 4, i16 = lane & 15;
+  const SeqList s = seq_list(a, b);
+  const int ns = num_splits_for(a, s.len);
+  if (split >= ns) return;
+  const int e_begin = split * a.split_tokens;
+  const int e_end = min(s.len, e_begin + a.split_tokens);
+  const int G = a.group_size, M = a.rows, Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+
+  // Q^T fragments, resident for the whole split.
+  u32x4 qf[NT][KS];
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    const int row = rt * 16 + i16;
+    if (row < M) {
+      const int r = row / G, h = g * G + row % G;
+      const uint16_t *qrow =
+          static_cast<const uint16_t *>(a.q) + ((size_t)(b * a.nrows + r) * Hq + h) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[rt][ks] = *reinterpret_cast<const u32x4 *>(qrow + (4 * ks + q4) * 8);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  f32x4 o[NT][DPL];
+  float m_run[NT], l_run[NT];
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    m_run[rt] = kMInit;
+    l_run[rt] = 0.f;
+#pragma unroll
+    for (int at = 0; at < DPL; ++at) o[rt][at] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const char *kc = static_cast<const char *>(a.k_cache);
+  const char *vc = static_cast<const char *>(a.v_cache);
+  const size_t slot_bytes = (size_t)Hkv * D * 2;
+  const size_t head_off = (size_t)g * D * 2;
+  const bool do_export = !a.sparse && (a.logits != nullptr || a.group != nullptr);
+  const bool vec_export = (a.max_prefix & 3) == 0;
+
+  const int ntiles = (e_end - e_begin + 31) / 32;
+  for (int t = wave; t < ntiles; t += kWaves) {
+    const int e0 = e_begin + t * 32;
+    // Slot of entry e0 + (lane & 31), then each lane picks the slots it loads.
+    const int my_e = min(e0 + (lane & 31), s.len - 1);
+    const int my_slot = entry_slot(a, b, s, my_e);
+    int kslot[2], vslot[8];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) kslot[tt] = __shfl(my_slot, tt * 16 + i16);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) vslot[v] = __shfl(my_slot, v < 4 ? 4 * q4 + v : 12 + 4 * q4 + v);
+
+    u32x4 kf[2][KS];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const char *krow = kc + (size_t)kslot[tt] * slot_bytes + head_off;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[tt][ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(krow + (4 * ks + q4) * 16));
+    }
+    VRow<D> vr[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const char *vrow = vc + (size_t)vslot[v] * slot_bytes + head_off + i16 * (DPL * 2);
+      if constexpr (D == 128)
+        vr[v].w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vrow));
+      else
+        vr[v].w = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(vrow));
+    }
+
+    // S^T = K Q^T
+    f32x4 st[2][NT];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[tt][ks]), as_bf16x8(qf[rt][ks]),
+                                                        acc, 0, 0, 0);
+        st[tt][rt] = acc;
+      }
+
+    // Logit export (verify): rows 0 and gamma, entries below the prefix length.
+    if (do_export && e0 < s.p_export) {
+      if (a.logits) {
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+          const int row = rt * 16 + i16;
+          if (row < M) {
+            const int r = row / G, h = g * G + row % G;
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+              if ((x == 0 && r == 0) || (x == 1 && r == a.gamma)) {
+                float *dst = a.logits + ((size_t)(b * 2 + x) * Hq + h) * a.max_prefix;
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                  const int e = e0 + tt * 16 + 4 * q4;
+                  const f32x4 lv = st[tt][rt] * a.scale;
+                  if (vec_export && e + 3 < s.p_export) {
+                    *reinterpret_cast<f32x4 *>(dst + e) = lv;
+                  } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                      if (e + c < s.p_export) dst[e + c] = lv[c];
+                  }
+                }
+              }
+            }
+          }
+        }
+      }
+      if (a.group) {
+        float *dst = a.group + (size_t)(b * Hkv + g) * a.max_prefix;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          f32x4 gs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int rt = 0; rt < NT; ++rt) {
+            const int row = rt * 16 + i16;
+            const int r = row / G;
+            const float w = (row < M) ? (float)((r == 0) + (r == a.gamma)) : 0.f;
+            gs += w * st[tt][rt];
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c) gs[c] = sum_within_group(gs[c]) * a.scale;
+          if (i16 == 0) {
+            const int e = e0 + tt * 16 + 4 * q4;
+            if (vec_export && e + 3 < s.p_export) {
+              *reinterpret_cast<f32x4 *>(dst + e) = gs;
+            } else {
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                if (e + c < s.p_export) dst[e + c] = gs[c];
+            }
+          }
+        }
+      }
+    }
+
+    // Online softmax (base 2) and P^T fragments.
+    bf16x8 pb[NT];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      const int row = rt * 16 + i16;
+      const int vis = s.vis0 + row / G;  // entries i < vis are visible to this row
+      float x[2][4];
+      float mx = kMInit;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int e = e0 + tt * 16 + 4 * q4 + c;
+          const bool ok = (e < e_end) && (e < vis);
+          x[tt][c] = ok ? st[tt][rt][c] * a.scale_log2 : kNegInf;
+          mx = fmaxf(mx, x[tt][c]);
+        }
+      mx = max_across_groups(mx);
+      const float m_new = fmaxf(m_run[rt], mx);
+      const float alpha = exp2_fast(m_run[rt] - m_new);
+      m_run[rt] = m_new;
+      float p[2][4];
+      float psum = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          p[tt][c] = exp2_fast(x[tt][c] - m_new);
+          psum += p[tt][c];
+        }
+      l_run[rt] = l_run[rt] * alpha + psum;
+#pragma unroll
+      for (int at = 0; at < DPL; ++at) o[rt][at] *= alpha;
+      u32x4 pk;
+      pk[0] = f32x2_to_bf16x2(p[0][0], p[0][1]);
+      pk[1] = f32x2_to_bf16x2(p[0][2], p[0][3]);
+      pk[2] = f32x2_to_bf16x2(p[1][0], p[1][1]);
+      pk[3] = f32x2_to_bf16x2(p[1][2], p[1][3]);
+      pb[rt] = as_bf16x8(pk);
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int at = 0; at < DPL; ++at) {
+      u32x4 va;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x0 = vr[2 * w].w[at >> 1], x1 = vr[2 * w + 1].w[at >> 1];
+        va[w] = (at & 1) ? pack_hi(x0, x1) : pack_lo(x0, x1);
+      }
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt)
+        o[rt][at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pb[rt], o[rt][at], 0, 0, 0);
+    }
+  }
+
+  // Merge the 4 waves' states into this split's partial.
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    const float lsum = sum_across_groups(l_run[rt]);
+    if (q4 == 0) {
+      sm.m[wave][rt * 16 + i16] = m_run[rt];
+      sm.l[wave][rt * 16 + i16] = lsum;
+    }
+  }
+  __syncthreads();
+  const size_t pidx = part_index(a, b, g, split);
+  merge_stats<ROWS, D>(sm, a.part_ml + pidx * 2, M);
+  // O^T tile `at`, register c holds row (rt*16 + i16), d = DPL*(4*q4 + c) + at.
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    float *orow = &sm.o[wave][rt * 16 + i16][0];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int d0 = DPL * (4 * q4 + c);
+#pragma unroll
+      for (int at = 0; at < DPL; at += 4)
+        *reinterpret_cast<f32x4 *>(orow + d0 + at) =
+            f32x4{o[rt][at][c], o[rt][at + 1][c], o[rt][at + 2][c], o[rt][at + 3][c]};
+    }
+  }
+  __syncthreads();
+  merge_o<ROWS, D>(sm, a.part_o + pidx * D, M);
+  if constexpr (FUSED) finish_split<D>(a, counters, b, g, ns, &sm_flag);
+}
+
+}  // namespace vg

@@ -1,0 +1,399 @@
+// vegas_attn.hip -- host side of the vegas_attn C-ABI: argument validation,
+// workspace layout, launch planning and kernel launches.  See
+// include/vegas_attn.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "vegas_attn.h"
+#include "attn_common.h"
+#include "attn_mfma.h"
+#include "attn_valu.h"
+#include "select.h"
+
+namespace {
+
+using namespace vg;
+
+constexpr size_t kAlign = 256;
+constexpr int kTargetWorkgroups = 512;  // two resident attention workgroups per CU on 256 CUs
+constexpr size_t kFusedCombineBytes = 128 * 1024;  // per (b, g) partial bytes a last workgroup merges
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+__global__ void zero_kernel(u32x4 *p, size_t n16, uint8_t *tail, size_t ntail) {
+  const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t j = i; j < n16; j += stride) p[j] = u32x4{0u, 0u, 0u, 0u};
+  if (i < ntail) tail[i] = 0;
+}
+
+bool valid_shape(const vg_shape *s) {
+  if (!s) return false;
+  if (s->batch < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1) return false;
+  if (s->num_q_heads % s->num_kv_heads) return false;
+  if (s->head_dim < 1 || s->page_size < 1 || s->max_pages_per_seq < 1) return false;
+  if (s->dtype != VG_DTYPE_F32 && s->dtype != VG_DTYPE_BF16) return false;
+  if (s->kernel < VG_KERNEL_AUTO || s->kernel > VG_KERNEL_MFMA) return false;
+  if (!std::isfinite(s->softmax_scale)) return false;
+  return true;
+}
+
+vg_status supported_shape(const vg_shape *s) {
+  if (s->head_dim != 64 && s->head_dim != 128) return VG_ERR_UNSUPPORTED;
+  if (s->page_size != kPageSize) return VG_ERR_UNSUPPORTED;
+  if (s->dtype == VG_DTYPE_F32 && s->kernel == VG_KERNEL_MFMA) return VG_ERR_UNSUPPORTED;
+  return VG_OK;
+}
+
+bool use_mfma(const vg_shape *s) {
+  return s->dtype == VG_DTYPE_BF16 && s->kernel != VG_KERNEL_VALU;
+}
+
+// Launch plan and workspace layout of one attention call.
+struct AttnPlan {
+  int rows, nt, mr, splits, split_tokens;
+  bool mfma, fused;
+  size_t off_part_o, off_part_ml, off_counters, bytes;
+};
+
+AttnPlan plan_attention(const vg_shape *s, int nrows, long long max_len, bool sparse) {
+  AttnPlan p{};
+  const int G = s->num_q_heads / s->num_kv_heads;
+  p.rows = nrows * G;
+  p.nt = (p.rows + 15) / 16;
+  p.mr = p.rows <= 16 ? 16 : (p.rows <= 32 ? 32 : 64);
+  p.mfma = use_mfma(s);
+  const int unit = p.mfma ? kWaves * 32 : kWaves * kWave;  // entries per workgroup pass
+  const long long bg = (long long)s->batch * s->num_kv_heads;
+  const long long len = max_len > 0 ? max_len : 1;
+  if (sparse) {
+    const long long mult = (len * bg) / ((long long)unit * 2048);
+    p.split_tokens = unit * (int)(mult > 1 ? mult : 1);
+  } else {
+    const long long per = (kTargetWorkgroups + bg - 1) / bg;
+    long long st = (len + per - 1) / per;
+    st = (st + unit - 1) / unit * unit;
+    p.split_tokens = (int)(st > unit ? st : unit);
+  }
+  p.splits = ceil_div(len, p.split_tokens);
+  const size_t n_part = (size_t)bg * p.splits * p.rows;
+  p.fused = (size_t)p.splits * p.rows * s->head_dim * 4 <= kFusedCombineBytes;
+  p.off_part_o = 0;
+  p.off_part_ml = align_up(n_part * s->head_dim * sizeof(float));
+  p.off_counters = p.off_part_ml + align_up(n_part * 2 * sizeof(float));
+  p.bytes = p.off_counters + align_up((size_t)bg * sizeof(uint32_t));
+  return p;
+}
+
+float effective_scale(const vg_shape *s) {
+  return s->softmax_scale > 0.f ? s->softmax_scale : 1.0f / std::sqrt((float)s->head_dim);
+}
+
+template <int D, int NT, bool FUSED>
+void launch_mfma_nt(const AttnArgs &a, uint32_t *ctr, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((attn_mfma_kernel<D, NT, FUSED>), grid, dim3(kThreads), 0, st, a, ctr);
+}
+
+template <int D, bool FUSED>
+void launch_mfma_d(int nt, const AttnArgs &a, uint32_t *ctr, dim3 grid, hipStream_t st) {
+  switch (nt) {
+    case 1: launch_mfma_nt<D, 1, FUSED>(a, ctr, grid, st); break;
+    case 2: launch_mfma_nt<D, 2, FUSED>(a, ctr, grid, st); break;
+    case 3: launch_mfma_nt<D, 3, FUSED>(a, ctr, grid, st); break;
+    default: launch_mfma_nt<D, 4, FUSED>(a, ctr, grid, st); break;
+  }
+}
+
+template <typename T, int D, bool FUSED>
+void launch_valu_t(int mr, const AttnArgs &a, uint32_t *ctr, dim3 grid, hipStream_t st) {
+  switch (mr) {
+    case 16: hipLaunchKernelGGL((attn_valu_kernel<T, D, 16, FUSED>), grid, dim3(kThreads), 0, st, a, ctr); break;
+    case 32: hipLaunchKernelGGL((attn_valu_kernel<T, D, 32, FUSED>), grid, dim3(kThreads), 0, st, a, ctr); break;
+    default: hipLaunchKernelGGL((attn_valu_kernel<T, D, 64, FUSED>), grid, dim3(kThreads), 0, st, a, ctr); break;
+  }
+}
+
+template <bool FUSED>
+void launch_attn_fused(const vg_shape *s, const AttnPlan &p, const AttnArgs &a, uint32_t *ctr,
+                       hipStream_t st) {
+  const dim3 grid(p.splits, s->num_kv_heads, s->batch);
+  if (p.mfma) {
+    if (s->head_dim == 128) launch_mfma_d<128, FUSED>(p.nt, a, ctr, grid, st);
+    else launch_mfma_d<64, FUSED>(p.nt, a, ctr, grid, st);
+  } else if (s->dtype == VG_DTYPE_BF16) {
+    if (s->head_dim == 128) launch_valu_t<uint16_t, 128, FUSED>(p.mr, a, ctr, grid, st);
+    else launch_valu_t<uint16_t, 64, FUSED>(p.mr, a, ctr, grid, st);
+  } else {
+    if (s->head_dim == 128) launch_valu_t<float, 128, FUSED>(p.mr, a, ctr, grid, st);
+    else launch_valu_t<float, 64, FUSED>(p.mr, a, ctr, grid, st);
+  }
+}
+
+vg_status launch_attention(const vg_shape *s, const AttnPlan &p, AttnArgs &a, char *ws,
+                           hipStream_t st) {
+  a.part_o = reinterpret_cast<float *>(ws + p.off_part_o);
+  a.part_ml = reinterpret_cast<float *>(ws + p.off_part_ml);
+  uint32_t *ctr = reinterpret_cast<uint32_t *>(ws + p.off_counters);
+  a.splits = p.splits;
+  a.split_tokens = p.split_tokens;
+  a.rows = p.rows;
+  if (p.fused) {
+    launch_attn_fused<true>(s, p, a, ctr, st);
+  } else {
+    launch_attn_fused<false>(s, p, a, ctr, st);
+    const dim3 cgrid(ceil_div((long long)p.rows * s->head_dim, 4 * 256), s->num_kv_heads, s->batch);
+    if (s->head_dim == 128)
+      hipLaunchKernelGGL((combine_kernel<128>), cgrid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((combine_kernel<64>), cgrid, dim3(256), 0, st, a);
+  }
+  return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- topk workspace
+struct SelPlan {
+  size_t off_hist, off_done, off_ccount, off_stage, bytes;
+};
+
+SelPlan plan_select(int batch, int max_prefix) {
+  SelPlan p{};
+  p.off_hist = 0;
+  p.off_done = align_up((size_t)batch * kBins1 * sizeof(uint32_t));
+  p.off_ccount = p.off_done + align_up((size_t)batch * sizeof(uint32_t));
+  p.off_stage = p.off_ccount + align_up((size_t)batch * kMaxChunks * sizeof(int32_t));
+  p.bytes = p.off_stage + align_up((size_t)batch * (size_t)(max_prefix > 0 ? max_prefix : 1) * 8);
+  return p;
+}
+
+SelWs sel_ws(const SelPlan &p, void *ws) {
+  char *c = static_cast<char *>(ws);
+  SelWs w;
+  w.hist1 = reinterpret_cast<uint32_t *>(c + p.off_hist);
+  w.done = reinterpret_cast<uint32_t *>(c + p.off_done);
+  w.ccount = reinterpret_cast<int32_t *>(c + p.off_ccount);
+  w.stage = reinterpret_cast<u32x2 *>(c + p.off_stage);
+  return w;
+}
+
+constexpr int kMaxSelectPrefix = kMaxChunks * kChunk;
+
+}  // namespace
+
+extern "C" {
+
+const char *vg_status_string(vg_status status) {
+  switch (status) {
+    case VG_OK: return "VG_OK";
+    case VG_ERR_INVALID_ARG: return "VG_ERR_INVALID_ARG";
+    case VG_ERR_UNSUPPORTED: return "VG_ERR_UNSUPPORTED";
+    case VG_ERR_WORKSPACE: return "VG_ERR_WORKSPACE";
+    case VG_ERR_HIP: return "VG_ERR_HIP";
+    default: return "VG_ERR_UNKNOWN";
+  }
+}
+
+const char *vg_version(void) { return "vegas_attn 0.1 (gfx950)"; }
+
+vg_status vg_workspace_zero(void *workspace, size_t bytes, void *stream) {
+  if (bytes == 0) return VG_OK;
+  if (!workspace || !aligned16(workspace)) return VG_ERR_INVALID_ARG;
+  const size_t n16 = bytes / 16, ntail = bytes % 16;
+  uint8_t *tail = static_cast<uint8_t *>(workspace) + n16 * 16;
+  const int blocks = (int)std::min<size_t>(4096, (n16 + 255) / 256 + 1);
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<u32x4 *>(workspace), n16, tail, ntail);
+  return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
+}
+
+vg_status vg_verify_workspace_size(const vg_shape *shape, int32_t max_prefix, int32_t gamma,
+                                   size_t *bytes) {
+  if (!bytes || !valid_shape(shape) || max_prefix < 0 || gamma < 0 || gamma > 15)
+    return VG_ERR_INVALID_ARG;
+  const vg_status sup = supported_shape(shape);
+  if (sup != VG_OK) return sup;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  if ((gamma + 1) * G > kMaxRows) return VG_ERR_UNSUPPORTED;
+  *bytes = plan_attention(shape, gamma + 1, (long long)max_prefix + gamma + 1, false).bytes;
+  return VG_OK;
+}
+
+vg_status vg_verify_attention(const vg_shape *shape, const void *q, const void *k_cache,
+                              const void *v_cache, const int32_t *page_table,
+                              const int32_t *prefix_len, int32_t max_prefix, int32_t gamma,
+                              float *out, float *logits, float *group_scores, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  if (!valid_shape(shape) || max_prefix < 0 || gamma < 0 || gamma > 15) return VG_ERR_INVALID_ARG;
+  const void *req[] = {q, k_cache, v_cache, page_table, prefix_len, out};
+  for (const void *p : req)
+    if (!p || !aligned16(p)) return VG_ERR_INVALID_ARG;
+  if (!logits && !group_scores) return VG_ERR_INVALID_ARG;
+  if ((logits && !aligned16(logits)) || (group_scores && !aligned16(group_scores)))
+    return VG_ERR_INVALID_ARG;
+  const vg_status sup = supported_shape(shape);
+  if (sup != VG_OK) return sup;
+  const int R = gamma + 1;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  if (R * G > kMaxRows) return VG_ERR_UNSUPPORTED;
+  if (ceil_div((long long)max_prefix + R, shape->page_size) > shape->max_pages_per_seq)
+    return VG_ERR_INVALID_ARG;
+  const AttnPlan p = plan_attention(shape, R, (long long)max_prefix + R, false);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < p.bytes) return VG_ERR_WORKSPACE;
+  AttnArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.page_table = page_table;
+  a.prefix_len = prefix_len;
+  a.out = out;
+  a.logits = logits;
+  a.group = group_scores;
+  a.max_pages = shape->max_pages_per_seq;
+  a.max_prefix = max_prefix;
+  a.nrows = R;
+  a.gamma = gamma;
+  a.num_q_heads = shape->num_q_heads;
+  a.num_kv_heads = shape->num_kv_heads;
+  a.group_size = G;
+  a.scale = effective_scale(shape);
+  a.scale_log2 = a.scale * kLog2e;
+  a.sparse = 0;
+  return launch_attention(shape, p, a, static_cast<char *>(workspace),
+                          static_cast<hipStream_t>(stream));
+}
+
+vg_status vg_aggregate_scores(int32_t batch, const float *src, int32_t src_rows, int32_t src_heads,
+                              const int32_t *prefix_len, int32_t max_prefix, float *scores,
+                              void *select_ws, size_t select_ws_bytes, void *stream) {
+  if (batch < 1 || src_rows < 1 || src_heads < 1 || max_prefix < 0) return VG_ERR_INVALID_ARG;
+  if (!src || !prefix_len || !scores || !aligned16(src) || !aligned16(prefix_len) ||
+      !aligned16(scores))
+    return VG_ERR_INVALID_ARG;
+  if (max_prefix > kMaxSelectPrefix) return VG_ERR_UNSUPPORTED;
+  SelArgs a{};
+  a.batch = batch;
+  a.max_prefix = max_prefix;
+  a.prefix_len = prefix_len;
+  a.scores_out = scores;
+  a.src = src;
+  a.src_rows = src_rows;
+  a.src_heads = src_heads;
+  if (max_prefix == 0) return VG_OK;
+  const dim3 grid(ceil_div(max_prefix, kChunk), batch);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (select_ws) {
+    const SelPlan p = plan_select(batch, max_prefix);
+    if (!aligned16(select_ws) || select_ws_bytes < p.bytes) return VG_ERR_WORKSPACE;
+    a.ws = sel_ws(p, select_ws);
+    hipLaunchKernelGGL((select_pass1_kernel<true, true>), grid, dim3(kSelThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((select_pass1_kernel<true, false>), grid, dim3(kSelThreads), 0, st, a);
+  }
+  return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
+}
+
+vg_status vg_topk_workspace_size(int32_t batch, int32_t max_prefix, size_t *bytes) {
+  if (!bytes || batch < 1 || max_prefix < 0) return VG_ERR_INVALID_ARG;
+  if (max_prefix > kMaxSelectPrefix) return VG_ERR_UNSUPPORTED;
+  *bytes = plan_select(batch, max_prefix).bytes;
+  return VG_OK;
+}
+
+vg_status vg_topk_select(int32_t batch, const float *scores, int32_t max_prefix,
+                         const int32_t *prefix_len, const int32_t *k, int32_t max_k,
+                         const int32_t *page_table, int32_t page_size, int32_t max_pages_per_seq,
+                         int32_t *sel_pos, int32_t *sel_slot, int32_t *sel_count, int32_t flags,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  if (batch < 1 || max_prefix < 0 || max_k < 0) return VG_ERR_INVALID_ARG;
+  if (flags != 0 && flags != VG_TOPK_PREPASS_DONE) return VG_ERR_INVALID_ARG;
+  const void *req[] = {scores, prefix_len, k, sel_pos, sel_count};
+  for (const void *p : req)
+    if (!p || !aligned16(p)) return VG_ERR_INVALID_ARG;
+  if (sel_slot && (!aligned16(sel_slot) || !page_table || !aligned16(page_table) ||
+                   page_size < 1 || max_pages_per_seq < 1 ||
+                   ceil_div(max_prefix, page_size) > max_pages_per_seq))
+    return VG_ERR_INVALID_ARG;
+  if (max_prefix > kMaxSelectPrefix) return VG_ERR_UNSUPPORTED;
+  const SelPlan p = plan_select(batch, max_prefix);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < p.bytes) return VG_ERR_WORKSPACE;
+  SelArgs a{};
+  a.batch = batch;
+  a.max_prefix = max_prefix;
+  a.max_k = max_k;
+  a.prefix_len = prefix_len;
+  a.k = k;
+  a.scores = scores;
+  a.page_table = page_table;
+  a.page_size = page_size;
+  a.max_pages = max_pages_per_seq;
+  a.sel_pos = sel_pos;
+  a.sel_slot = sel_slot;
+  a.sel_count = sel_count;
+  a.ws = sel_ws(p, workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(ceil_div(max_prefix > 0 ? max_prefix : 1, kChunk), batch);
+  if (!(flags & VG_TOPK_PREPASS_DONE))
+    hipLaunchKernelGGL((select_pass1_kernel<false, true>), grid, dim3(kSelThreads), 0, st, a);
+  hipLaunchKernelGGL(select_pass2_kernel, grid, dim3(kSelThreads), 0, st, a);
+  return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
+}
+
+vg_status vg_sparse_draft_workspace_size(const vg_shape *shape, int32_t n_q, int32_t max_k,
+                                         int32_t max_tail, size_t *bytes) {
+  if (!bytes || !valid_shape(shape) || n_q < 1 || max_k < 0 || max_tail < n_q)
+    return VG_ERR_INVALID_ARG;
+  const vg_status sup = supported_shape(shape);
+  if (sup != VG_OK) return sup;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  if (n_q * G > kMaxRows) return VG_ERR_UNSUPPORTED;
+  *bytes = plan_attention(shape, n_q, (long long)max_k + max_tail, true).bytes;
+  return VG_OK;
+}
+
+vg_status vg_sparse_draft_attention(const vg_shape *shape, const void *q, int32_t n_q,
+                                    const void *k_cache, const void *v_cache,
+                                    const int32_t *sel_slot, const int32_t *sel_count,
+                                    int32_t max_k, const int32_t *page_table,
+                                    const int32_t *tail_start, const int32_t *tail_len,
+                                    int32_t max_tail, float *out, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+  if (!valid_shape(shape) || n_q < 1 || max_k < 0 || max_tail < n_q) return VG_ERR_INVALID_ARG;
+  const void *req[] = {q, k_cache, v_cache, sel_count, page_table, tail_start, tail_len, out};
+  for (const void *p : req)
+    if (!p || !aligned16(p)) return VG_ERR_INVALID_ARG;
+  if (max_k > 0 && (!sel_slot || !aligned16(sel_slot))) return VG_ERR_INVALID_ARG;
+  const vg_status sup = supported_shape(shape);
+  if (sup != VG_OK) return sup;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  if (n_q * G > kMaxRows) return VG_ERR_UNSUPPORTED;
+  const AttnPlan p = plan_attention(shape, n_q, (long long)max_k + max_tail, true);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < p.bytes) return VG_ERR_WORKSPACE;
+  AttnArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.page_table = page_table;
+  a.sel_slot = sel_slot;
+  a.sel_count = sel_count;
+  a.tail_start = tail_start;
+  a.tail_len = tail_len;
+  a.out = out;
+  a.max_pages = shape->max_pages_per_seq;
+  a.max_k = max_k;
+  a.nrows = n_q;
+  a.gamma = 0;
+  a.num_q_heads = shape->num_q_heads;
+  a.num_kv_heads = shape->num_kv_heads;
+  a.group_size = G;
+  a.scale = effective_scale(shape);
+  a.scale_log2 = a.scale * kLog2e;
+  a.sparse = 1;
+  return launch_attention(shape, p, a, static_cast<char *>(workspace),
+                          static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+// vg_device.h -- device-side types and helpers shared by the vegas_attn kernels
+// (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+// Running-max start value: finite, so exp2(m_old - m_new) stays 0 or 1 and never NaN.
+constexpr float kMInit = -1.0e30f;
+constexpr int kPageSize = 16;
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Exponential in base 2 (hardware v_exp_f32).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sum / max across the 4 sixteen-lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float sum_across_groups(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+__device__ __forceinline__ float max_across_groups(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+// Sum across the 16 lanes of a group (lanes sharing l / 16).
+__device__ __forceinline__ float sum_within_group(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Arguments of one attention launch (verify or sparse draft).  The keys that
+// (sequence b, KV head g) attends form a list of length L_b:
+//   entries [0, cnt_b)    come from an explicit slot list (sparse: sel_slot),
+//   entries [cnt_b, L_b)  are positions base_b + (i - cnt_b) translated through
+//                         the page table (verify: the whole cache; sparse: the tail).
+// Query row r (of nrows) sees entries i < L_b - nrows + 1 + r.
+// Verify additionally exports the logits of rows 0 and gamma for entries i < P_b.
+struct AttnArgs {
+  const void *q;            // [B][nrows][Hq][D]
+  const void *k_cache;      // [slots][Hkv][D]
+  const void *v_cache;      // [slots][Hkv][D]
+  const int32_t *page_table;  // [B][max_pages]
+  const int32_t *sel_slot;    // [B][max_k] (sparse) or null
+  const int32_t *sel_count;   // [B] (sparse) or null
+  const int32_t *prefix_len;  // [B] (verify) or null
+  const int32_t *tail_start;  // [B] (sparse) or null
+  const int32_t *tail_len;    // [B] (sparse) or null
+  float *out;               // [B][nrows][Hq][D]
+  float *logits;            // [B][2][Hq][max_prefix] or null
+  float *group;             // [B][Hkv][max_prefix] or null
+  float *part_o;            // [B][Hkv][splits][M][D]
+  float *part_ml;           // [B][Hkv][splits][M][2]
+  int32_t max_pages, max_k, max_prefix;
+  int32_t nrows, gamma;
+  int32_t num_q_heads, num_kv_heads, group_size, rows;  // rows = M = nrows * G
+  int32_t splits, split_tokens;
+  float scale;       // logit = scale * q.k (natural-log units)
+  float scale_log2;  // scale * log2(e)
+  int32_t sparse;
+};
+
+struct SeqList {
+  int cnt, base, len, vis0, p_export;
+};
+
+__device__ __forceinline__ SeqList seq_list(const AttnArgs &a, int b) {
+  SeqList s;
+  if (a.sparse) {
+    s.cnt = a.sel_count[b];
+    s.base = a.tail_start[b];
+    s.len = s.cnt + a.tail_len[b];
+    s.p_export = 0;
+  } else {
+    s.cnt = 0;
+    s.base = 0;
+    s.p_export = a.prefix_len[b];
+    s.len = s.p_export + a.nrows;
+  }
+  s.vis0 = s.len - a.nrows + 1;
+  return s;
+}
+
+// Physical slot of list entry i (0 <= i < len).
+__device__ __forceinline__ int32_t entry_slot(const AttnArgs &a, int b, const SeqList &s, int i) {
+  if (i < s.cnt) return a.sel_slot[(size_t)b * a.max_k + i];
+  int pos = s.base + (i - s.cnt);
+  return a.page_table[(size_t)b * a.max_pages + (pos >> 4)] * kPageSize + (pos & (kPageSize - 1));
+}
+
+__device__ __forceinline__ int num_splits_for(const AttnArgs &a, int len) {
+  int n = (len + a.split_tokens - 1) / a.split_tokens;
+  return n < a.splits ? n : a.splits;
+}
+
+}  // namespace vg

@@ -1,0 +1,116 @@
+"""Device plumbing around the C-ABI: put a seeded workload in HBM, allocate
+outputs and workspaces, and run the path's steps in order.
+
+PyTorch is used only for device memory, streams and events; every step of
+the path is a call into libvegas_attn.so.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _binding as vg
+from .synth import Case
+
+
+def _dev(a: np.ndarray, device) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)  # bf16 bit patterns travel as int16
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class DeviceCase:
+    """One workload resident on the GPU, with every buffer the path writes."""
+
+    def __init__(self, case: Case, device="cuda", kernel=vg.VG_KERNEL_AUTO, max_tail=None):
+        self.case = case
+        self.device = torch.device(device)
+        dev = self.device
+        c = case
+        self.B, self.Hq, self.Hkv, self.D = c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim
+        self.gamma, self.R = c.gamma, c.rows
+        self.max_prefix, self.max_k = c.max_prefix, max(c.max_k, 1)
+        self.dtype = vg.VG_DTYPE_BF16 if c.dtype == "bf16" else vg.VG_DTYPE_F32
+        self.shape = vg.make_shape(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                   c.max_pages, self.dtype, c.scale, kernel, c.page_size)
+        self.q = _dev(c.q, dev)
+        self.q_draft = _dev(c.q_draft, dev)  # [gamma][B][Hq][D]
+        self.k_cache = _dev(c.k_cache, dev)
+        self.v_cache = _dev(c.v_cache, dev)
+        self.page_table = _dev(c.page_table, dev)
+        self.prefix_len = _dev(c.prefix_len, dev)
+        self.k = _dev(c.k, dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        mp = max(self.max_prefix, 1)
+        self.out = torch.zeros(self.B, self.R, self.Hq, self.D, **f32)
+        self.logits = torch.zeros(self.B, 2, self.Hq, mp, **f32)
+        self.group = torch.zeros(self.B, self.Hkv, mp, **f32)
+        self.scores = torch.zeros(self.B, mp, **f32)
+        self.sel_pos = torch.full((self.B, self.max_k), -1, **i32)
+        self.sel_slot = torch.full((self.B, self.max_k), -1, **i32)
+        self.sel_count = torch.zeros(self.B, **i32)
+        self.draft_out = torch.zeros(self.B, 1, self.Hq, self.D, **f32)
+        self.tail_start = self.prefix_len.clone()
+        self.max_tail = int(max_tail) if max_tail is not None else self.R
+        self.tail_len = [torch.full((self.B,), s + 1, **i32) for s in range(max(self.gamma, 1))]
+        self.ws_verify_bytes = vg.vg_verify_workspace_size(self.shape, self.max_prefix, self.gamma)
+        self.ws_select_bytes = vg.vg_topk_workspace_size(self.B, self.max_prefix)
+        self.ws_sparse_bytes = vg.vg_sparse_draft_workspace_size(self.shape, 1, self.max_k, self.max_tail)
+        self.ws_verify = self._workspace(self.ws_verify_bytes)
+        self.ws_select = self._workspace(self.ws_select_bytes)
+        self.ws_sparse = self._workspace(self.ws_sparse_bytes)
+
+    def _workspace(self, nbytes):
+        ws = torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=self.device)
+        vg.vg_workspace_zero(ws, ws.numel())
+        return ws
+
+    # ------------------------------------------------------------------ steps
+    def verify(self, export="both", stream=None):
+        logits = self.logits if export in ("raw", "both") else None
+        group = self.group if export in ("group", "both") else None
+        vg.vg_verify_attention(self.shape, self.q, self.k_cache, self.v_cache, self.page_table,
+                               self.prefix_len, self.max_prefix, self.gamma, self.out, logits, group,
+                               self.ws_verify, self.ws_verify_bytes, stream)
+
+    def aggregate(self, src="raw", fuse_prepass=False, stream=None):
+        if src == "raw":
+            t, rows, heads = self.logits, 2, self.Hq
+        else:
+            t, rows, heads = self.group, 1, self.Hkv
+        ws = self.ws_select if fuse_prepass else None
+        vg.vg_aggregate_scores(self.B, t, rows, heads, self.prefix_len, self.max_prefix, self.scores,
+                               ws, self.ws_select_bytes if fuse_prepass else 0, stream)
+
+    def topk(self, scores=None, prepass_done=False, stream=None):
+        flags = vg.VG_TOPK_PREPASS_DONE if prepass_done else 0
+        vg.vg_topk_select(self.B, self.scores if scores is None else scores, self.max_prefix,
+                          self.prefix_len, self.k, self.max_k, self.page_table, self.case.page_size,
+                          self.case.max_pages, self.sel_pos, self.sel_slot, self.sel_count, flags,
+                          self.ws_select, self.ws_select_bytes, stream)
+
+    def sparse(self, step=0, q=None, sel_slot=None, sel_count=None, tail_start=None, tail_len=None,
+               out=None, n_q=1, stream=None):
+        qq = self.q_draft[step] if q is None else q
+        vg.vg_sparse_draft_attention(
+            self.shape, qq, n_q, self.k_cache, self.v_cache,
+            self.sel_slot if sel_slot is None else sel_slot,
+            self.sel_count if sel_count is None else sel_count,
+            self.max_k, self.page_table,
+            self.tail_start if tail_start is None else tail_start,
+            self.tail_len[step] if tail_len is None else tail_len,
+            self.max_tail, self.draft_out if out is None else out,
+            self.ws_sparse, self.ws_sparse_bytes, stream)
+
+    def iteration(self, export="group", stream=None):
+        """One pass of the whole path: verify (+export), aggregate, top-k, gamma draft steps."""
+        self.verify(export=export, stream=stream)
+        self.aggregate(src="group" if export == "group" else "raw", fuse_prepass=True, stream=stream)
+        self.topk(prepass_done=True, stream=stream)
+        for s in range(self.gamma):
+            self.sparse(step=s, stream=stream)
+
+    # ------------------------------------------------------------- host copies
+    def host(self, name):
+        return getattr(self, name).detach().cpu().numpy()
