@@ -1,0 +1,299 @@
+"""Benchmark of the vegas_attn hot path on one MI355X.
+
+A step is one Vegas decode iteration of the attention work of an L-layer
+stack of the configured layer (default: the Qwen3-8B-shaped layer at 128K
+context, gamma = 6, k = 4% of the prefix):
+
+    for s in 0..gamma-1:  for each layer: sparse draft attention (draft step s)
+    for each layer:       verify attention + group-sum export, aggregation with
+                          the fused first radix pass, exact top-k
+
+Each layer has its own KV cache copy in HBM, so no layer's data is still in
+the 256 MB MALL when it is read again: every byte counted below is an HBM
+byte.  Inputs are seeded synthetic tensors, resident in HBM before timing.
+
+Printed: one JSON line with the whole-step achieved HBM GB/s (algorithmic
+bytes / time), ms per step, per-layer us per iteration, the roofline of the
+dominant kernel (verify attention, timed with HIP events around every verify
+call inside the timed region) and the fp64 CPU oracle timed on a bounded
+sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Achieved HBM GB/s & us/iter, verify+select+sparse-draft attention at 128K ctx"
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_traffic.json")
+
+
+def algorithmic_bytes(c, export):
+    """Bytes the method must move per layer iteration (measurement)."""
+    s_kv = 2 if c.dtype == "bf16" else 4
+    row = c.num_kv_heads * c.head_dim * s_kv  # one token, all KV heads, K or V
+    N = c.prefix_len.astype(np.int64) + c.rows
+    P = c.prefix_len.astype(np.int64)
+    kk = np.minimum(c.k, c.prefix_len).astype(np.int64)
+    q_bytes = c.batch * c.rows * c.num_q_heads * c.head_dim * s_kv
+    out_bytes = c.batch * c.rows * c.num_q_heads * c.head_dim * 4
+    exp_rows = c.num_kv_heads if export == "group" else 2 * c.num_q_heads
+    export_bytes = int(P.sum()) * exp_rows * 4
+    verify = int(N.sum()) * 2 * row + q_bytes + out_bytes + export_bytes
+    aggregate = export_bytes + int(P.sum()) * 4
+    topk = int(P.sum()) * 4 + int(kk.sum()) * 8
+    draft = []
+    for s in range(c.gamma):
+        keys = int((kk + s + 1).sum())
+        draft.append(keys * 2 * row + c.batch * c.num_q_heads * c.head_dim * (s_kv + 4))
+    return dict(verify=verify, aggregate=aggregate, topk=topk, draft=draft,
+                total=verify + aggregate + topk + sum(draft))
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "verification_guided_sparse_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel_hash):
+    """HBM bytes per verify launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = d.get(workload)
+    if not e or e.get("kernel_hash") != kernel_hash:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(c, export, nthreads):
+    """The fp64 oracle on the host cores: one full layer iteration of the workload."""
+    import oracle
+    t0 = time.perf_counter()
+    out, logits, group, _ = oracle.verify(c.q, c.k_cache, c.v_cache, c.page_table, c.prefix_len,
+                                          c.gamma, c.scale, nthreads=nthreads)
+    s = oracle.aggregate(group if export == "group" else logits, c.prefix_len)
+    pos, slot, cnt = oracle.topk(s, c.prefix_len, c.k, page_table=c.page_table)
+    for st in range(c.gamma):
+        oracle.sparse(np.ascontiguousarray(c.q_draft[st][:, None]), c.k_cache, c.v_cache,
+                      c.page_table, pos, cnt, c.prefix_len, np.full(c.batch, st + 1, np.int32),
+                      c.scale, nthreads=nthreads)
+    return time.perf_counter() - t0
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3_qwen3_128k")
+    ap.add_argument("--layers", type=int, default=0, help="layer copies (0: enough to exceed the MALL)")
+    ap.add_argument("--export", choices=["group", "raw"], default="group")
+    ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="also time every step separately")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs the path on a single MI355X; "
+              "run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from verification_guided_sparse_amd import _binding as vg
+    from verification_guided_sparse_amd import synth
+    from verification_guided_sparse_amd.runner import DeviceCase
+
+    vg.lib()  # fail loudly if the HIP library is missing
+    kernel = {"auto": vg.VG_KERNEL_AUTO, "valu": vg.VG_KERNEL_VALU, "mfma": vg.VG_KERNEL_MFMA}[args.kernel]
+    c = synth.make_case(args.workload)
+    ab = algorithmic_bytes(c, args.export)
+    layer_kv = int((c.prefix_len.astype(np.int64) + c.rows).sum()) * c.num_kv_heads * c.head_dim * 2 * (
+        2 if c.dtype == "bf16" else 4)
+    L = args.layers or max(2, int(np.ceil(3 * 256e6 / max(sum(ab["draft"]) / max(c.gamma, 1), 1))))
+    L = min(L, max(2, int(40e9 // layer_kv)))
+    print(f"[bench] {args.workload}: {L} layers, {layer_kv / 1e6:.1f} MB KV per layer, "
+          f"export={args.export}, kernel={args.kernel}", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    layers = [DeviceCase(c, device=dev, kernel=kernel)]
+    for _ in range(L - 1):
+        layers.append(DeviceCase(c, device=dev, kernel=kernel, like=layers[0]))
+
+    def step():
+        for s in range(c.gamma):
+            for lc in layers:
+                lc.sparse(step=s)
+        for lc in layers:
+            lc.verify(export=args.export)
+            lc.aggregate(src=args.export, fuse_prepass=True)
+            lc.topk(prepass_done=True)
+
+    # the first draft step needs a selection: run one eager iteration per layer
+    for lc in layers:
+        lc.iteration(export=args.export)
+    torch.cuda.synchronize()
+    # one step = one HIP graph (no host launch overhead inside the timed region)
+    g_step = capture(step)
+    g_verify = capture(lambda: [lc.verify(export=args.export) for lc in layers])
+    for _ in range(args.warmup):
+        g_step.replay()
+    torch.cuda.synchronize()
+
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    v_start, v_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for k in range(args.steps):
+        g_step.replay()
+    t_end.record()
+    # the dominant kernel: every layer's verify call, back to back, same graph form
+    v_start.record()
+    for k in range(args.steps):
+        g_verify.replay()
+    v_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    verify_us = 1e3 * v_start.elapsed_time(v_end) / (args.steps * L)
+
+    bytes_per_step = ab["total"] * L
+    value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    achieved = ab["verify"] / (verify_us * 1e-6) / 1e9
+    khash = kernel_source_hash()
+    traffic = measured_traffic(args.workload, khash)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if c.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "batch": c.batch,
+            "prefix": [int(x) for x in c.prefix_len] if c.batch <= 8 else int(c.max_prefix),
+            "heads": f"{c.num_q_heads}q/{c.num_kv_heads}kv",
+            "head_dim": c.head_dim,
+            "gamma": c.gamma,
+            "k": [int(x) for x in c.k],
+            "layers_per_step": L,
+            "export": args.export,
+            "kernel": args.kernel,
+            "parallelism": "single-gpu",
+        },
+        "us_per_iter": round(1e3 * ms_per_step / L, 2),
+        "roofline": {
+            "kernel": "vg_verify_attention",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "verify_us": round(verify_us, 2),
+            "algorithmic_bytes_per_launch": ab["verify"],
+        },
+        "wall_s_timed": round(wall, 3),
+    }
+
+    if args.breakdown:
+        result["breakdown_us"] = breakdown(layers, c, args.export)
+
+    if not args.no_cpu_baseline:
+        nthreads = min(16, os.cpu_count() or 1)
+        t = cpu_baseline(c, args.export, nthreads)
+        result["cpu_baseline"] = {
+            "value": round(ab["total"] / t / 1e9, 4),
+            "unit": "GB/s",
+            "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"one full {args.workload} layer iteration (verify, aggregate, top-k, "
+                      f"{c.gamma} draft steps) in fp64, {t:.2f} s",
+        }
+    print(json.dumps(result), flush=True)
+
+
+def capture(fn):
+    """Record fn's launches into a HIP graph (torch.cuda.CUDAGraph on ROCm)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm the launch path outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def breakdown(layers, c, export):
+    """Per-call durations: each call kind over all layers captured in its own graph,
+    replayed and timed with HIP events; reported per call (us)."""
+    import torch
+    reps = 5
+    kinds = {
+        "verify": lambda: [lc.verify(export=export) for lc in layers],
+        "verify_no_export": lambda: [lc.verify(export="none") for lc in layers],
+        "aggregate": lambda: [lc.aggregate(src=export, fuse_prepass=True) for lc in layers],
+        "topk_after_prepass": lambda: [lc.topk(prepass_done=True) for lc in layers],
+        "draft": lambda: [lc.sparse(step=c.gamma - 1) for lc in layers],
+    }
+    out = {}
+    for name, fn in kinds.items():
+        if name == "topk_after_prepass":
+            # the prepass must precede every top-k: time (aggregate + topk) and subtract
+            g = capture(lambda: [(lc.aggregate(src=export, fuse_prepass=True), lc.topk(prepass_done=True))
+                                 for lc in layers])
+        else:
+            g = capture(fn)
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = 1e3 * a.elapsed_time(b) / (reps * len(layers))
+    out["topk"] = out.pop("topk_after_prepass") - out["aggregate"]
+    out = {k: round(v, 2) for k, v in out.items()}
+    out["overhead_frac"] = round((out["verify"] - out["verify_no_export"] + out["aggregate"] + out["topk"])
+                                 / out["verify_no_export"], 4)
+    # restore a consistent selection for later replays
+    for lc in layers:
+        lc.iteration(export=export)
+    torch.cuda.synchronize()
+    return out
+
+
+if __name__ == "__main__":
+    main()

@@ -124,7 +124,7 @@ vg_status vg_verify_workspace_size(const vg_shape *shape, int32_t max_prefix, in
  *                scale applied); entries j >= P_b are not written.
  *   group_scores [B][Hkv][max_prefix] float, nullable: sum over the G query
  *                heads of KV head g of both exported rows, for j < P_b.
- *   At least one of logits / group_scores must be non-null.
+ *   Both exports may be null (plain causal attention, no export).
  * Supported: D in {64, 128}; page_size 16; (gamma+1)*G <= 64; bf16 with any
  * kernel, f32 with VG_KERNEL_VALU or AUTO.
  */

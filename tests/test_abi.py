@@ -69,9 +69,9 @@ def test_verify_rejects_before_launch():
     sh = _shape(max_pages_per_seq=100)
     fake = 0x10000  # 16-byte aligned, never dereferenced on these paths
     args = [fake] * 5
-    # logits and group both NULL
+    # null output
     with pytest.raises(vg.VgError) as e:
-        vg.vg_verify_attention(sh, *args, 1000, 4, fake, None, None, fake, 1 << 30, 0)
+        vg.vg_verify_attention(sh, *args, 1000, 4, None, None, None, fake, 1 << 30, 0)
     assert e.value.status == vg.VG_ERR_INVALID_ARG
     # misaligned q
     with pytest.raises(vg.VgError) as e:
@@ -114,3 +114,11 @@ def test_topk_and_sparse_reject_before_launch():
     with pytest.raises(vg.VgError) as e:  # null sel_slot with max_k > 0
         vg.vg_sparse_draft_attention(sh, fake, 1, fake, fake, None, fake, 10, fake, fake, fake, 2, fake, fake, 1 << 30, 0)
     assert e.value.status == vg.VG_ERR_INVALID_ARG
+
+
+def test_oversized_key_lists_rejected():
+    """More keys than the split bookkeeping can hold is reported, not truncated."""
+    sh = _shape(max_pages_per_seq=1 << 20)
+    with pytest.raises(vg.VgError) as e:
+        vg.vg_sparse_draft_workspace_size(sh, 1, 600_000, 8)
+    assert e.value.status == vg.VG_ERR_UNSUPPORTED

@@ -239,3 +239,42 @@ def test_full_size_parity(torch_cuda, name):
     c = synth.make_case(name)
     dc, refs = _run_steps(c)
     _run_chain(c, dc, refs, "group")
+
+
+def test_graph_replay_matches_eager(torch_cuda):
+    """One iteration captured in a HIP graph and replayed several times, with eager
+    work and synchronisations between replays: every replay equals the eager run."""
+    import torch
+    from verification_guided_sparse_amd.runner import DeviceCase
+    c = synth.make_case(synth.small("c5_gptoss_64k", prefix=(2500, 1200)))
+    dc = DeviceCase(c)
+    names = ("out", "group", "scores", "sel_pos", "sel_slot", "sel_count", "draft_out")
+    dc.iteration(export="group")
+    torch.cuda.synchronize()
+    eager = [dc.host(n).copy() for n in names]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dc.iteration(export="group")
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        dc.iteration(export="group")
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for n in names:
+            getattr(dc, n).fill_(-7)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = {n: dc.host(n) for n in names}
+        ref = dict(zip(names, eager))
+        for n in ("out", "sel_count", "draft_out"):
+            assert np.array_equal(got[n], ref[n]), (rep, n)
+        for b in range(c.batch):  # entries the contract writes
+            P, k = int(c.prefix_len[b]), int(ref["sel_count"][b])
+            assert np.array_equal(got["group"][b, :, :P], ref["group"][b, :, :P]), (rep, b)
+            assert np.array_equal(got["scores"][b, :P], ref["scores"][b, :P]), (rep, b)
+            assert np.array_equal(got["sel_pos"][b, :k], ref["sel_pos"][b, :k]), (rep, b)
+            assert np.array_equal(got["sel_slot"][b, :k], ref["sel_slot"][b, :k]), (rep, b)

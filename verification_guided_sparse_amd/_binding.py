@@ -11,7 +11,7 @@ import ctypes as C
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libvegas_attn.so")
+LIB_PATH = os.environ.get("VG_LIB_PATH") or os.path.join(_HERE, "libvegas_attn.so")
 
 VG_OK = 0
 VG_ERR_INVALID_ARG = 1

@@ -56,12 +56,226 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-template <int D, int NT, bool FUSED>
-__global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, uint32_t *counters) {
+// One 32-entry tile of K and V for this lane (see the layout notes above).
+template <int D>
+struct KVTile {
+  u32x4 kf[2][D / 32];
+  VRow<D> vr[8];
+};
+
+// Slots of a split's entries, staged in LDS once per workgroup so that the
+// tile loop issues its K/V loads without a dependent page-table load first.
+//   verify: page ids of the split's pages (entry e -> slot_sm[e/16 - page0] * 16 + e % 16)
+//   sparse: the explicit slot list of the split (entries below cnt)
+constexpr int kSlotSm = 1024;
+
+__device__ __forceinline__ void stage_slots(int *slot_sm, const AttnArgs &a, int b, const SeqList &s,
+                                            int e_begin, int e_end) {
+  if (!a.sparse) {
+    const int p0 = e_begin >> 4, p1 = (e_end - 1) >> 4;
+    for (int i = threadIdx.x; i <= p1 - p0; i += kThreads)
+      slot_sm[i] = a.page_table[(size_t)b * a.max_pages + p0 + i];
+  } else {
+    const int n = min(e_end, s.cnt) - e_begin;
+    for (int i = threadIdx.x; i < n; i += kThreads)
+      slot_sm[i] = a.sel_slot[(size_t)b * a.max_k + e_begin + i];
+  }
+}
+
+__device__ __forceinline__ int staged_slot(const int *slot_sm, const AttnArgs &a, int b,
+                                           const SeqList &s, int e_begin, int e) {
+  if (!a.sparse) return slot_sm[(e >> 4) - (e_begin >> 4)] * kPageSize + (e & (kPageSize - 1));
+  if (e < s.cnt) return slot_sm[e - e_begin];
+  return entry_slot(a, b, s, e);  // causal tail: a few positions through the page table
+}
+
+template <int D>
+__device__ __forceinline__ void load_tile(KVTile<D> &T, const AttnArgs &a, int b, const SeqList &s,
+                                          int e0, int g, int lane, const int *slot_sm, int e_begin,
+                                          int e_end) {
+  constexpr int KS = D / 32, DPL = D / 16;
+  const int q4 = lane >> 4, i16 = lane & 15;
+  const size_t slot_bytes = (size_t)a.num_kv_heads * D * 2;
+  const size_t head_off = (size_t)g * D * 2;
+  // slot of entry e0 + (lane & 31); each lane then picks the slots it loads.
+  // Entries past the split's end (masked later) reuse its last entry, whose
+  // slot is staged.
+  const int my_e = min(e0 + (lane & 31), e_end - 1);
+  const int my_slot = staged_slot(slot_sm, a, b, s, e_begin, my_e);
+  const char *kc = static_cast<const char *>(a.k_cache);
+  const char *vc = static_cast<const char *>(a.v_cache);
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int ks_slot = __shfl(my_slot, tt * 16 + i16);
+    const char *krow = kc + (size_t)ks_slot * slot_bytes + head_off;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      T.kf[tt][ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(krow + (4 * ks + q4) * 16));
+  }
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int vs = __shfl(my_slot, v < 4 ? 4 * q4 + v : 12 + 4 * q4 + v);
+    const char *vrow = vc + (size_t)vs * slot_bytes + head_off + i16 * (DPL * 2);
+    if constexpr (D == 128)
+      T.vr[v].w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vrow));
+    else
+      T.vr[v].w = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(vrow));
+  }
+}
+
+template <int D, int NT>
+struct WaveState {
+  u32x4 qf[NT][D / 32];  // Q^T fragments (B operand of S^T = K Q^T)
+  f32x4 o[NT][D / 16];   // O^T accumulators
+  float m_run[NT], l_run[NT];
+};
+
+template <int D, int NT>
+__device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D> &T,
+                                             const AttnArgs &a, int b, int g, const SeqList &s,
+                                             int e0, int e_end, int lane, bool do_export,
+                                             bool vec_export) {
+  constexpr int KS = D / 32, DPL = D / 16;
+  const int q4 = lane >> 4, i16 = lane & 15;
+  const int G = a.group_size, M = a.rows, Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+
+  // S^T = K Q^T
+  f32x4 st[2][NT];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(T.kf[tt][ks]), as_bf16x8(W.qf[rt][ks]),
+                                                      acc, 0, 0, 0);
+      st[tt][rt] = acc;
+    }
+
+  // Logit export (verify): rows 0 and gamma, entries below the prefix length.
+  if (do_export && e0 < s.p_export) {
+    if (a.logits) {
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        const int row = rt * 16 + i16;
+        if (row < M) {
+          const int r = row / G, h = g * G + row % G;
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            if ((x == 0 && r == 0) || (x == 1 && r == a.gamma)) {
+              float *dst = a.logits + ((size_t)(b * 2 + x) * Hq + h) * a.max_prefix;
+#pragma unroll
+              for (int tt = 0; tt < 2; ++tt) {
+                const int e = e0 + tt * 16 + 4 * q4;
+                const f32x4 lv = st[tt][rt] * a.scale;
+                if (vec_export && e + 3 < s.p_export) {
+                  *reinterpret_cast<f32x4 *>(dst + e) = lv;
+                } else {
+#pragma unroll
+                  for (int c = 0; c < 4; ++c)
+                    if (e + c < s.p_export) dst[e + c] = lv[c];
+                }
+              }
+            }
+          }
+        }
+      }
+    }
+    if (a.group) {
+      float *dst = a.group + (size_t)(b * Hkv + g) * a.max_prefix;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        f32x4 gs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+          const int row = rt * 16 + i16;
+          const int r = row / G;
+          const float w = (row < M) ? (float)((r == 0) + (r == a.gamma)) : 0.f;
+          gs += w * st[tt][rt];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) gs[c] = sum_within_group(gs[c]) * a.scale;
+        if (i16 == 0) {
+          const int e = e0 + tt * 16 + 4 * q4;
+          if (vec_export && e + 3 < s.p_export) {
+            *reinterpret_cast<f32x4 *>(dst + e) = gs;
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (e + c < s.p_export) dst[e + c] = gs[c];
+          }
+        }
+      }
+    }
+  }
+
+  // Online softmax (base 2) and P^T fragments.
+  bf16x8 pb[NT];
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    const int row = rt * 16 + i16;
+    const int vis = s.vis0 + row / G;  // entries i < vis are visible to this row
+    float x[2][4];
+    float mx = kMInit;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e = e0 + tt * 16 + 4 * q4 + c;
+        const bool ok = (e < e_end) && (e < vis);
+        x[tt][c] = ok ? st[tt][rt][c] * a.scale_log2 : kNegInf;
+        mx = fmaxf(mx, x[tt][c]);
+      }
+    mx = max_across_groups(mx);
+    const float m_new = fmaxf(W.m_run[rt], mx);
+    const float alpha = exp2_fast(W.m_run[rt] - m_new);
+    W.m_run[rt] = m_new;
+    float p[2][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        p[tt][c] = exp2_fast(x[tt][c] - m_new);
+        psum += p[tt][c];
+      }
+    W.l_run[rt] = W.l_run[rt] * alpha + psum;
+#pragma unroll
+    for (int at = 0; at < DPL; ++at) W.o[rt][at] *= alpha;
+    u32x4 pk;
+    pk[0] = f32x2_to_bf16x2(p[0][0], p[0][1]);
+    pk[1] = f32x2_to_bf16x2(p[0][2], p[0][3]);
+    pk[2] = f32x2_to_bf16x2(p[1][0], p[1][1]);
+    pk[3] = f32x2_to_bf16x2(p[1][2], p[1][3]);
+    pb[rt] = as_bf16x8(pk);
+  }
+
+  // O^T += V^T P^T
+#pragma unroll
+  for (int at = 0; at < DPL; ++at) {
+    u32x4 va;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t x0 = T.vr[2 * w].w[at >> 1], x1 = T.vr[2 * w + 1].w[at >> 1];
+      va[w] = (at & 1) ? pack_hi(x0, x1) : pack_lo(x0, x1);
+    }
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+      W.o[rt][at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pb[rt], W.o[rt][at], 0, 0, 0);
+  }
+}
+
+// PF = tiles in flight per wave: 1 (load, then compute; two waves per SIMD)
+// or 2 (the next tile loads while this one computes; one wave per SIMD).
+template <int D, int NT, bool FUSED, int PF>
+__global__ __launch_bounds__(kThreads, PF == 1 ? 2 : 1) void attn_mfma_kernel(AttnArgs a,
+                                                                             uint32_t *counters) {
   constexpr int KS = D / 32;   // k-steps of the QK^T contraction
   constexpr int DPL = D / 16;  // d values per lane per V row, = number of PV tiles
   constexpr int ROWS = NT * 16;
   __shared__ MergeSmem<ROWS, D> sm;
+  __shared__ int slot_sm[kSlotSm];
   __shared__ int sm_flag;
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -72,10 +286,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, uint
   if (split >= ns) return;
   const int e_begin = split * a.split_tokens;
   const int e_end = min(s.len, e_begin + a.split_tokens);
-  const int G = a.group_size, M = a.rows, Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int G = a.group_size, M = a.rows, Hq = a.num_q_heads;
+  stage_slots(slot_sm, a, b, s, e_begin, e_end);
 
-  // Q^T fragments, resident for the whole split.
-  u32x4 qf[NT][KS];
+  WaveState<D, NT> W;
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
     const int row = rt * 16 + i16;
@@ -85,193 +299,59 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, uint
           static_cast<const uint16_t *>(a.q) + ((size_t)(b * a.nrows + r) * Hq + h) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        qf[rt][ks] = *reinterpret_cast<const u32x4 *>(qrow + (4 * ks + q4) * 8);
+        W.qf[rt][ks] = *reinterpret_cast<const u32x4 *>(qrow + (4 * ks + q4) * 8);
     } else {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = u32x4{0u, 0u, 0u, 0u};
+      for (int ks = 0; ks < KS; ++ks) W.qf[rt][ks] = u32x4{0u, 0u, 0u, 0u};
     }
+    W.m_run[rt] = kMInit;
+    W.l_run[rt] = 0.f;
+#pragma unroll
+    for (int at = 0; at < DPL; ++at) W.o[rt][at] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  f32x4 o[NT][DPL];
-  float m_run[NT], l_run[NT];
-#pragma unroll
-  for (int rt = 0; rt < NT; ++rt) {
-    m_run[rt] = kMInit;
-    l_run[rt] = 0.f;
-#pragma unroll
-    for (int at = 0; at < DPL; ++at) o[rt][at] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const char *kc = static_cast<const char *>(a.k_cache);
-  const char *vc = static_cast<const char *>(a.v_cache);
-  const size_t slot_bytes = (size_t)Hkv * D * 2;
-  const size_t head_off = (size_t)g * D * 2;
   const bool do_export = !a.sparse && (a.logits != nullptr || a.group != nullptr);
   const bool vec_export = (a.max_prefix & 3) == 0;
+  __syncthreads();  // slot_sm ready
 
+  // This wave's tiles: j = 0 .. nw-1 cover entries e_begin + 32 * (wave + 4 j).
   const int ntiles = (e_end - e_begin + 31) / 32;
-  for (int t = wave; t < ntiles; t += kWaves) {
-    const int e0 = e_begin + t * 32;
-    // Slot of entry e0 + (lane & 31), then each lane picks the slots it loads.
-    const int my_e = min(e0 + (lane & 31), s.len - 1);
-    const int my_slot = entry_slot(a, b, s, my_e);
-    int kslot[2], vslot[8];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) kslot[tt] = __shfl(my_slot, tt * 16 + i16);
-#pragma unroll
-    for (int v = 0; v < 8; ++v) vslot[v] = __shfl(my_slot, v < 4 ? 4 * q4 + v : 12 + 4 * q4 + v);
-
-    u32x4 kf[2][KS];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const char *krow = kc + (size_t)kslot[tt] * slot_bytes + head_off;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[tt][ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(krow + (4 * ks + q4) * 16));
+  const int nw = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  auto e_of = [&](int j) { return e_begin + 32 * (wave + kWaves * j); };
+  if constexpr (PF == 1) {
+    for (int j = 0; j < nw; ++j) {
+      KVTile<D> A;
+      load_tile<D>(A, a, b, s, e_of(j), g, lane, slot_sm, e_begin, e_end);
+      compute_tile<D, NT>(W, A, a, b, g, s, e_of(j), e_end, lane, do_export, vec_export);
     }
-    VRow<D> vr[8];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const char *vrow = vc + (size_t)vslot[v] * slot_bytes + head_off + i16 * (DPL * 2);
-      if constexpr (D == 128)
-        vr[v].w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vrow));
-      else
-        vr[v].w = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(vrow));
-    }
-
-    // S^T = K Q^T
-    f32x4 st[2][NT];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int rt = 0; rt < NT; ++rt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[tt][ks]), as_bf16x8(qf[rt][ks]),
-                                                        acc, 0, 0, 0);
-        st[tt][rt] = acc;
-      }
-
-    // Logit export (verify): rows 0 and gamma, entries below the prefix length.
-    if (do_export && e0 < s.p_export) {
-      if (a.logits) {
-#pragma unroll
-        for (int rt = 0; rt < NT; ++rt) {
-          const int row = rt * 16 + i16;
-          if (row < M) {
-            const int r = row / G, h = g * G + row % G;
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-              if ((x == 0 && r == 0) || (x == 1 && r == a.gamma)) {
-                float *dst = a.logits + ((size_t)(b * 2 + x) * Hq + h) * a.max_prefix;
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                  const int e = e0 + tt * 16 + 4 * q4;
-                  const f32x4 lv = st[tt][rt] * a.scale;
-                  if (vec_export && e + 3 < s.p_export) {
-                    *reinterpret_cast<f32x4 *>(dst + e) = lv;
-                  } else {
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                      if (e + c < s.p_export) dst[e + c] = lv[c];
-                  }
-                }
-              }
-            }
-          }
-        }
-      }
-      if (a.group) {
-        float *dst = a.group + (size_t)(b * Hkv + g) * a.max_prefix;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          f32x4 gs = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int rt = 0; rt < NT; ++rt) {
-            const int row = rt * 16 + i16;
-            const int r = row / G;
-            const float w = (row < M) ? (float)((r == 0) + (r == a.gamma)) : 0.f;
-            gs += w * st[tt][rt];
-          }
-#pragma unroll
-          for (int c = 0; c < 4; ++c) gs[c] = sum_within_group(gs[c]) * a.scale;
-          if (i16 == 0) {
-            const int e = e0 + tt * 16 + 4 * q4;
-            if (vec_export && e + 3 < s.p_export) {
-              *reinterpret_cast<f32x4 *>(dst + e) = gs;
-            } else {
-#pragma unroll
-              for (int c = 0; c < 4; ++c)
-                if (e + c < s.p_export) dst[e + c] = gs[c];
-            }
-          }
-        }
-      }
-    }
-
-    // Online softmax (base 2) and P^T fragments.
-    bf16x8 pb[NT];
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt) {
-      const int row = rt * 16 + i16;
-      const int vis = s.vis0 + row / G;  // entries i < vis are visible to this row
-      float x[2][4];
-      float mx = kMInit;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int e = e0 + tt * 16 + 4 * q4 + c;
-          const bool ok = (e < e_end) && (e < vis);
-          x[tt][c] = ok ? st[tt][rt][c] * a.scale_log2 : kNegInf;
-          mx = fmaxf(mx, x[tt][c]);
-        }
-      mx = max_across_groups(mx);
-      const float m_new = fmaxf(m_run[rt], mx);
-      const float alpha = exp2_fast(m_run[rt] - m_new);
-      m_run[rt] = m_new;
-      float p[2][4];
-      float psum = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          p[tt][c] = exp2_fast(x[tt][c] - m_new);
-          psum += p[tt][c];
-        }
-      l_run[rt] = l_run[rt] * alpha + psum;
-#pragma unroll
-      for (int at = 0; at < DPL; ++at) o[rt][at] *= alpha;
-      u32x4 pk;
-      pk[0] = f32x2_to_bf16x2(p[0][0], p[0][1]);
-      pk[1] = f32x2_to_bf16x2(p[0][2], p[0][3]);
-      pk[2] = f32x2_to_bf16x2(p[1][0], p[1][1]);
-      pk[3] = f32x2_to_bf16x2(p[1][2], p[1][3]);
-      pb[rt] = as_bf16x8(pk);
-    }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int at = 0; at < DPL; ++at) {
-      u32x4 va;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x0 = vr[2 * w].w[at >> 1], x1 = vr[2 * w + 1].w[at >> 1];
-        va[w] = (at & 1) ? pack_hi(x0, x1) : pack_lo(x0, x1);
-      }
-#pragma unroll
-      for (int rt = 0; rt < NT; ++rt)
-        o[rt][at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pb[rt], o[rt][at], 0, 0, 0);
-    }
+  } else {
+  // Two tiles in flight: tile j+1 loads while tile j computes.  In the steady
+  // state every iteration issues its loads unconditionally, so the wait before
+  // a tile covers exactly that tile's (older) loads.
+  KVTile<D> A, B;
+  if (nw > 0) load_tile<D>(A, a, b, s, e_of(0), g, lane, slot_sm, e_begin, e_end);
+  if (nw > 1) load_tile<D>(B, a, b, s, e_of(1), g, lane, slot_sm, e_begin, e_end);
+  int j = 0;
+  for (; j + 3 < nw; j += 2) {
+    compute_tile<D, NT>(W, A, a, b, g, s, e_of(j), e_end, lane, do_export, vec_export);
+    load_tile<D>(A, a, b, s, e_of(j + 2), g, lane, slot_sm, e_begin, e_end);
+    compute_tile<D, NT>(W, B, a, b, g, s, e_of(j + 1), e_end, lane, do_export, vec_export);
+    load_tile<D>(B, a, b, s, e_of(j + 3), g, lane, slot_sm, e_begin, e_end);
+  }
+  if (j < nw) {
+    compute_tile<D, NT>(W, A, a, b, g, s, e_of(j), e_end, lane, do_export, vec_export);
+    if (j + 2 < nw) load_tile<D>(A, a, b, s, e_of(j + 2), g, lane, slot_sm, e_begin, e_end);
+  }
+  if (j + 1 < nw) compute_tile<D, NT>(W, B, a, b, g, s, e_of(j + 1), e_end, lane, do_export, vec_export);
+  if (j + 2 < nw) compute_tile<D, NT>(W, A, a, b, g, s, e_of(j + 2), e_end, lane, do_export, vec_export);
   }
 
   // Merge the 4 waves' states into this split's partial.
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
-    const float lsum = sum_across_groups(l_run[rt]);
+    const float lsum = sum_across_groups(W.l_run[rt]);
     if (q4 == 0) {
-      sm.m[wave][rt * 16 + i16] = m_run[rt];
+      sm.m[wave][rt * 16 + i16] = W.m_run[rt];
       sm.l[wave][rt * 16 + i16] = lsum;
     }
   }
@@ -288,12 +368,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(AttnArgs a, uint
 #pragma unroll
       for (int at = 0; at < DPL; at += 4)
         *reinterpret_cast<f32x4 *>(orow + d0 + at) =
-            f32x4{o[rt][at][c], o[rt][at + 1][c], o[rt][at + 2][c], o[rt][at + 3][c]};
+            f32x4{W.o[rt][at][c], W.o[rt][at + 1][c], W.o[rt][at + 2][c], W.o[rt][at + 3][c]};
     }
   }
   __syncthreads();
   merge_o<ROWS, D>(sm, a.part_o + pidx * D, M);
-  if constexpr (FUSED) finish_split<D>(a, counters, b, g, ns, &sm_flag);
+  if constexpr (FUSED) {
+    __syncthreads();  // the merge area becomes combine scratch
+    finish_split<D>(a, counters, b, g, ns, &sm_flag, &sm.o[0][0][0]);
+  }
 }
 
 }  // namespace vg

@@ -189,7 +189,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_valu_kernel(AttnArgs a, uint
     for (int k = 0; k < DV; ++k) sm.merge.o[wave][m][lane * DV + k] = o[m][k];
   __syncthreads();
   merge_o<MR, D>(sm.merge, a.part_o + pidx * D, M);
-  if constexpr (FUSED) finish_split<D>(a, counters, b, g, ns, &sm_flag);
+  if constexpr (FUSED) {
+    __syncthreads();  // the merge area becomes combine scratch
+    finish_split<D>(a, counters, b, g, ns, &sm_flag, &sm.merge.o[0][0][0]);
+  }
 }
 
 }  // namespace vg

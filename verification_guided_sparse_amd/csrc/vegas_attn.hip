@@ -18,8 +18,18 @@ namespace {
 using namespace vg;
 
 constexpr size_t kAlign = 256;
-constexpr int kTargetWorkgroups = 512;  // two resident attention workgroups per CU on 256 CUs
-constexpr size_t kFusedCombineBytes = 128 * 1024;  // per (b, g) partial bytes a last workgroup merges
+#ifndef VG_TARGET_WGS
+#define VG_TARGET_WGS 512
+#endif
+constexpr int kTargetWorkgroups = VG_TARGET_WGS;  // verify: two resident workgroups per CU on 256 CUs
+// Partial bytes per (b, g) up to which the last split workgroup combines in the
+// same launch.  0: the combine is always its own launch -- a workgroup-to-
+// workgroup handoff inside one launch needs a device-scope release, which on
+// gfx950 writes back the whole L2 from every workgroup.
+#ifndef VG_FUSED_COMBINE_BYTES
+#define VG_FUSED_COMBINE_BYTES 0
+#endif
+constexpr size_t kFusedCombineBytes = VG_FUSED_COMBINE_BYTES;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -57,7 +67,7 @@ bool use_mfma(const vg_shape *s) {
 // Launch plan and workspace layout of one attention call.
 struct AttnPlan {
   int rows, nt, mr, splits, split_tokens;
-  bool mfma, fused;
+  bool mfma, fused, ok;  // ok: the key list fits kMaxSplits splits
   size_t off_part_o, off_part_ml, off_counters, bytes;
 };
 
@@ -80,9 +90,17 @@ AttnPlan plan_attention(const vg_shape *s, int nrows, long long max_len, bool sp
     st = (st + unit - 1) / unit * unit;
     p.split_tokens = (int)(st > unit ? st : unit);
   }
+  // at most kMaxSplits splits per (b, g): the combine keeps their (m, l) in LDS
+  const long long min_st = ((len + kMaxSplits - 1) / kMaxSplits + unit - 1) / unit * unit;
+  if (p.split_tokens < min_st) p.split_tokens = (int)min_st;
+  // a split's slots (sparse) or page ids (verify) are staged in kSlotSm LDS
+  // entries; splits stay whole multiples of the workgroup pass
+  const long long max_st = (sparse ? kSlotSm : (long long)(kSlotSm - 1) * kPageSize) / unit * unit;
+  if (p.split_tokens > max_st) p.split_tokens = (int)max_st;
   p.splits = ceil_div(len, p.split_tokens);
+  p.ok = p.splits <= kMaxSplits;
   const size_t n_part = (size_t)bg * p.splits * p.rows;
-  p.fused = (size_t)p.splits * p.rows * s->head_dim * 4 <= kFusedCombineBytes;
+  p.fused = kFusedCombineBytes > 0 && (size_t)p.splits * p.rows * s->head_dim * 4 <= kFusedCombineBytes;
   p.off_part_o = 0;
   p.off_part_ml = align_up(n_part * s->head_dim * sizeof(float));
   p.off_counters = p.off_part_ml + align_up(n_part * 2 * sizeof(float));
@@ -94,9 +112,16 @@ float effective_scale(const vg_shape *s) {
   return s->softmax_scale > 0.f ? s->softmax_scale : 1.0f / std::sqrt((float)s->head_dim);
 }
 
+#ifndef VG_VERIFY_PF
+#define VG_VERIFY_PF 1
+#endif
+
 template <int D, int NT, bool FUSED>
 void launch_mfma_nt(const AttnArgs &a, uint32_t *ctr, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_mfma_kernel<D, NT, FUSED>), grid, dim3(kThreads), 0, st, a, ctr);
+  if (a.sparse)  // one tile per wave: no pipelining, two waves per SIMD
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NT, FUSED, 1>), grid, dim3(kThreads), 0, st, a, ctr);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NT, FUSED, VG_VERIFY_PF>), grid, dim3(kThreads), 0, st, a, ctr);
 }
 
 template <int D, bool FUSED>
@@ -146,37 +171,41 @@ vg_status launch_attention(const vg_shape *s, const AttnPlan &p, AttnArgs &a, ch
     launch_attn_fused<true>(s, p, a, ctr, st);
   } else {
     launch_attn_fused<false>(s, p, a, ctr, st);
-    const dim3 cgrid(ceil_div((long long)p.rows * s->head_dim, 4 * 256), s->num_kv_heads, s->batch);
+    const dim3 cgrid(p.rows, s->num_kv_heads, s->batch);
     if (s->head_dim == 128)
-      hipLaunchKernelGGL((combine_kernel<128>), cgrid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((combine_kernel<128>), cgrid, dim3(kThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((combine_kernel<64>), cgrid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((combine_kernel<64>), cgrid, dim3(kThreads), 0, st, a);
   }
   return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
 }
 
 // ---------------------------------------------------------------- topk workspace
 struct SelPlan {
-  size_t off_hist, off_done, off_ccount, off_stage, bytes;
+  size_t off_hist1, off_hist2, off_state, off_above, off_ncand, off_cand, bytes;
 };
 
 SelPlan plan_select(int batch, int max_prefix) {
   SelPlan p{};
-  p.off_hist = 0;
-  p.off_done = align_up((size_t)batch * kBins1 * sizeof(uint32_t));
-  p.off_ccount = p.off_done + align_up((size_t)batch * sizeof(uint32_t));
-  p.off_stage = p.off_ccount + align_up((size_t)batch * kMaxChunks * sizeof(int32_t));
-  p.bytes = p.off_stage + align_up((size_t)batch * (size_t)(max_prefix > 0 ? max_prefix : 1) * 8);
+  p.off_hist1 = 0;
+  p.off_hist2 = align_up((size_t)batch * kBins1 * sizeof(uint32_t));
+  p.off_state = p.off_hist2 + align_up((size_t)batch * kBins23 * sizeof(uint32_t));
+  p.off_above = p.off_state + align_up((size_t)batch * 4 * sizeof(int32_t));
+  p.off_ncand = p.off_above + align_up((size_t)batch * kMaxChunks * sizeof(int32_t));
+  p.off_cand = p.off_ncand + align_up((size_t)batch * kMaxChunks * sizeof(int32_t));
+  p.bytes = p.off_cand + align_up((size_t)batch * (size_t)(max_prefix > 0 ? max_prefix : 1) * 8);
   return p;
 }
 
 SelWs sel_ws(const SelPlan &p, void *ws) {
   char *c = static_cast<char *>(ws);
   SelWs w;
-  w.hist1 = reinterpret_cast<uint32_t *>(c + p.off_hist);
-  w.done = reinterpret_cast<uint32_t *>(c + p.off_done);
-  w.ccount = reinterpret_cast<int32_t *>(c + p.off_ccount);
-  w.stage = reinterpret_cast<u32x2 *>(c + p.off_stage);
+  w.hist1 = reinterpret_cast<uint32_t *>(c + p.off_hist1);
+  w.hist2 = reinterpret_cast<uint32_t *>(c + p.off_hist2);
+  w.state = reinterpret_cast<int32_t *>(c + p.off_state);
+  w.above = reinterpret_cast<int32_t *>(c + p.off_above);
+  w.ncand = reinterpret_cast<int32_t *>(c + p.off_ncand);
+  w.cand = reinterpret_cast<u32x2 *>(c + p.off_cand);
   return w;
 }
 
@@ -218,7 +247,9 @@ vg_status vg_verify_workspace_size(const vg_shape *shape, int32_t max_prefix, in
   if (sup != VG_OK) return sup;
   const int G = shape->num_q_heads / shape->num_kv_heads;
   if ((gamma + 1) * G > kMaxRows) return VG_ERR_UNSUPPORTED;
-  *bytes = plan_attention(shape, gamma + 1, (long long)max_prefix + gamma + 1, false).bytes;
+  const AttnPlan p = plan_attention(shape, gamma + 1, (long long)max_prefix + gamma + 1, false);
+  if (!p.ok) return VG_ERR_UNSUPPORTED;
+  *bytes = p.bytes;
   return VG_OK;
 }
 
@@ -231,7 +262,6 @@ vg_status vg_verify_attention(const vg_shape *shape, const void *q, const void *
   const void *req[] = {q, k_cache, v_cache, page_table, prefix_len, out};
   for (const void *p : req)
     if (!p || !aligned16(p)) return VG_ERR_INVALID_ARG;
-  if (!logits && !group_scores) return VG_ERR_INVALID_ARG;
   if ((logits && !aligned16(logits)) || (group_scores && !aligned16(group_scores)))
     return VG_ERR_INVALID_ARG;
   const vg_status sup = supported_shape(shape);
@@ -242,6 +272,7 @@ vg_status vg_verify_attention(const vg_shape *shape, const void *q, const void *
   if (ceil_div((long long)max_prefix + R, shape->page_size) > shape->max_pages_per_seq)
     return VG_ERR_INVALID_ARG;
   const AttnPlan p = plan_attention(shape, R, (long long)max_prefix + R, false);
+  if (!p.ok) return VG_ERR_UNSUPPORTED;
   if (!workspace || !aligned16(workspace) || workspace_bytes < p.bytes) return VG_ERR_WORKSPACE;
   AttnArgs a{};
   a.q = q;
@@ -339,6 +370,7 @@ vg_status vg_topk_select(int32_t batch, const float *scores, int32_t max_prefix,
   if (!(flags & VG_TOPK_PREPASS_DONE))
     hipLaunchKernelGGL((select_pass1_kernel<false, true>), grid, dim3(kSelThreads), 0, st, a);
   hipLaunchKernelGGL(select_pass2_kernel, grid, dim3(kSelThreads), 0, st, a);
+  hipLaunchKernelGGL(select_pass3_kernel, grid, dim3(kSelThreads), 0, st, a);
   return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
 }
 
@@ -350,7 +382,9 @@ vg_status vg_sparse_draft_workspace_size(const vg_shape *shape, int32_t n_q, int
   if (sup != VG_OK) return sup;
   const int G = shape->num_q_heads / shape->num_kv_heads;
   if (n_q * G > kMaxRows) return VG_ERR_UNSUPPORTED;
-  *bytes = plan_attention(shape, n_q, (long long)max_k + max_tail, true).bytes;
+  const AttnPlan p = plan_attention(shape, n_q, (long long)max_k + max_tail, true);
+  if (!p.ok) return VG_ERR_UNSUPPORTED;
+  *bytes = p.bytes;
   return VG_OK;
 }
 
@@ -371,6 +405,7 @@ vg_status vg_sparse_draft_attention(const vg_shape *shape, const void *q, int32_
   const int G = shape->num_q_heads / shape->num_kv_heads;
   if (n_q * G > kMaxRows) return VG_ERR_UNSUPPORTED;
   const AttnPlan p = plan_attention(shape, n_q, (long long)max_k + max_tail, true);
+  if (!p.ok) return VG_ERR_UNSUPPORTED;
   if (!workspace || !aligned16(workspace) || workspace_bytes < p.bytes) return VG_ERR_WORKSPACE;
   AttnArgs a{};
   a.q = q;

@@ -22,7 +22,10 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
 class DeviceCase:
     """One workload resident on the GPU, with every buffer the path writes."""
 
-    def __init__(self, case: Case, device="cuda", kernel=vg.VG_KERNEL_AUTO, max_tail=None):
+    def __init__(self, case: Case, device="cuda", kernel=vg.VG_KERNEL_AUTO, max_tail=None,
+                 like: "DeviceCase | None" = None):
+        """`like`: another DeviceCase of the same workload whose inputs are copied on
+        the device (a separate copy of the KV cache, e.g. another layer)."""
         self.case = case
         self.device = torch.device(device)
         dev = self.device
@@ -33,13 +36,17 @@ class DeviceCase:
         self.dtype = vg.VG_DTYPE_BF16 if c.dtype == "bf16" else vg.VG_DTYPE_F32
         self.shape = vg.make_shape(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
                                    c.max_pages, self.dtype, c.scale, kernel, c.page_size)
-        self.q = _dev(c.q, dev)
-        self.q_draft = _dev(c.q_draft, dev)  # [gamma][B][Hq][D]
-        self.k_cache = _dev(c.k_cache, dev)
-        self.v_cache = _dev(c.v_cache, dev)
-        self.page_table = _dev(c.page_table, dev)
-        self.prefix_len = _dev(c.prefix_len, dev)
-        self.k = _dev(c.k, dev)
+        if like is None:
+            self.q = _dev(c.q, dev)
+            self.q_draft = _dev(c.q_draft, dev)  # [gamma][B][Hq][D]
+            self.k_cache = _dev(c.k_cache, dev)
+            self.v_cache = _dev(c.v_cache, dev)
+            self.page_table = _dev(c.page_table, dev)
+            self.prefix_len = _dev(c.prefix_len, dev)
+            self.k = _dev(c.k, dev)
+        else:
+            for n in ("q", "q_draft", "k_cache", "v_cache", "page_table", "prefix_len", "k"):
+                setattr(self, n, getattr(like, n).clone())
         f32 = dict(dtype=torch.float32, device=dev)
         i32 = dict(dtype=torch.int32, device=dev)
         mp = max(self.max_prefix, 1)
