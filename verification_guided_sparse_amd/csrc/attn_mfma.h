@@ -16,9 +16,14 @@
 //
 // Lane l = 16*q4 + i16.  MFMA 16x16x32 operands: lane holds A[i16][8*q4 .. +7]
 // and B[8*q4 .. +7][i16]; the result C[4*q4 + c][i16], c = 0..3.
-//  * K: lane loads 16 bytes of token (tt*16 + i16), d-chunk 4*ks + q4.  The
-//    contraction over d may visit d in any order as long as Q uses the same
-//    one, so the four q4 lanes of a token read 64 contiguous bytes.
+//  * K: rows are read whole (CH = D/8 lanes x 16 bytes per row, 64/CH rows
+//    per instruction) and parked in a per-wave LDS tile whose rows are padded
+//    to D*2 + 16 bytes, so that both this write and the operand read are free
+//    of bank conflicts.  The operand read gives lane (q4, i16) token
+//    tt*16 + i16, d-chunk 4*ks + q4: the contraction over d may visit d in any
+//    order as long as Q uses the same one.  (Reading K straight into operand
+//    layout makes 64-byte fragments per token and measurably less HBM
+//    bandwidth than whole-row reads.)
 //  * V: lane loads d-chunk i16 of the 8 tokens tok(q4, v); 16 lanes cover one
 //    full 256-byte (D = 128) or 128-byte (D = 64) row per instruction.  Their
 //    8 x 8 (or 8 x 4) bf16 are repacked with byte permutes so that MFMA tile
@@ -59,8 +64,15 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
 // One 32-entry tile of K and V for this lane (see the layout notes above).
 template <int D>
 struct KVTile {
-  u32x4 kf[2][D / 32];
+  u32x4 kraw[D / 16];  // whole-row K loads: instruction i holds rows i*(64/CH) + lane/CH
   VRow<D> vr[8];
+};
+
+// Per-wave LDS staging of one K tile: 32 rows padded to D*2 + 16 bytes.
+template <int D>
+struct KStage {
+  static constexpr int kRowBytes = D * 2 + 16;
+  char rows[32 * kRowBytes];
 };
 
 // Slots of a split's entries, staged in LDS once per workgroup so that the
@@ -93,7 +105,7 @@ template <int D>
 __device__ __forceinline__ void load_tile(KVTile<D> &T, const AttnArgs &a, int b, const SeqList &s,
                                           int e0, int g, int lane, const int *slot_sm, int e_begin,
                                           int e_end) {
-  constexpr int KS = D / 32, DPL = D / 16;
+  constexpr int DPL = D / 16;
   const int q4 = lane >> 4, i16 = lane & 15;
   const size_t slot_bytes = (size_t)a.num_kv_heads * D * 2;
   const size_t head_off = (size_t)g * D * 2;
@@ -104,13 +116,14 @@ __device__ __forceinline__ void load_tile(KVTile<D> &T, const AttnArgs &a, int b
   const int my_slot = staged_slot(slot_sm, a, b, s, e_begin, my_e);
   const char *kc = static_cast<const char *>(a.k_cache);
   const char *vc = static_cast<const char *>(a.v_cache);
+  constexpr int CH = D / 8;       // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;    // rows per instruction
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int ks_slot = __shfl(my_slot, tt * 16 + i16);
-    const char *krow = kc + (size_t)ks_slot * slot_bytes + head_off;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      T.kf[tt][ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(krow + (4 * ks + q4) * 16));
+  for (int i = 0; i < D / 16; ++i) {
+    const int row = i * RPI + lane / CH;
+    const int ks_slot = __shfl(my_slot, row);
+    const char *krow = kc + (size_t)ks_slot * slot_bytes + head_off + (lane % CH) * 16;
+    T.kraw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(krow));
   }
 #pragma unroll
   for (int v = 0; v < 8; ++v) {
@@ -132,12 +145,31 @@ struct WaveState {
 
 template <int D, int NT>
 __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D> &T,
-                                             const AttnArgs &a, int b, int g, const SeqList &s,
-                                             int e0, int e_end, int lane, bool do_export,
-                                             bool vec_export) {
+                                             KStage<D> &ks_sm, const AttnArgs &a, int b, int g,
+                                             const SeqList &s, int e0, int e_end, int lane,
+                                             bool do_export, bool vec_export) {
   constexpr int KS = D / 32, DPL = D / 16;
+  constexpr int CH = D / 8, RPI = 64 / CH, RB = KStage<D>::kRowBytes;
   const int q4 = lane >> 4, i16 = lane & 15;
   const int G = a.group_size, M = a.rows, Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+
+  // K rows -> LDS -> operand layout (this wave's staging area only)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    const int row = i * RPI + lane / CH;
+    *reinterpret_cast<u32x4 *>(ks_sm.rows + row * RB + (lane % CH) * 16) = T.kraw[i];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  u32x4 kf[2][KS];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[tt][ks] = *reinterpret_cast<const u32x4 *>(ks_sm.rows + (tt * 16 + i16) * RB + (4 * ks + q4) * 16);
 
   // S^T = K Q^T
   f32x4 st[2][NT];
@@ -148,7 +180,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(T.kf[tt][ks]), as_bf16x8(W.qf[rt][ks]),
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[tt][ks]), as_bf16x8(W.qf[rt][ks]),
                                                       acc, 0, 0, 0);
       st[tt][rt] = acc;
     }
@@ -274,7 +306,11 @@ __global__ __launch_bounds__(kThreads, PF == 1 ? 2 : 1) void attn_mfma_kernel(At
   constexpr int KS = D / 32;   // k-steps of the QK^T contraction
   constexpr int DPL = D / 16;  // d values per lane per V row, = number of PV tiles
   constexpr int ROWS = NT * 16;
-  __shared__ MergeSmem<ROWS, D> sm;
+  __shared__ union {
+    KStage<D> kst[kWaves];   // during the tile loop
+    MergeSmem<ROWS, D> m;    // after it
+  } lds;
+  MergeSmem<ROWS, D> &sm = lds.m;
   __shared__ int slot_sm[kSlotSm];
   __shared__ int sm_flag;
 
@@ -322,7 +358,7 @@ __global__ __launch_bounds__(kThreads, PF == 1 ? 2 : 1) void attn_mfma_kernel(At
     for (int j = 0; j < nw; ++j) {
       KVTile<D> A;
       load_tile<D>(A, a, b, s, e_of(j), g, lane, slot_sm, e_begin, e_end);
-      compute_tile<D, NT>(W, A, a, b, g, s, e_of(j), e_end, lane, do_export, vec_export);
+      compute_tile<D, NT>(W, A, lds.kst[wave], a, b, g, s, e_of(j), e_end, lane, do_export, vec_export);
     }
   } else {
   // Two tiles in flight: tile j+1 loads while tile j computes.  In the steady
@@ -333,19 +369,20 @@ __global__ __launch_bounds__(kThreads, PF == 1 ? 2 : 1) void attn_mfma_kernel(At
   if (nw > 1) load_tile<D>(B, a, b, s, e_of(1), g, lane, slot_sm, e_begin, e_end);
   int j = 0;
   for (; j + 3 < nw; j += 2) {
-    compute_tile<D, NT>(W, A, a, b, g, s, e_of(j), e_end, lane, do_export, vec_export);
+    compute_tile<D, NT>(W, A, lds.kst[wave], a, b, g, s, e_of(j), e_end, lane, do_export, vec_export);
     load_tile<D>(A, a, b, s, e_of(j + 2), g, lane, slot_sm, e_begin, e_end);
-    compute_tile<D, NT>(W, B, a, b, g, s, e_of(j + 1), e_end, lane, do_export, vec_export);
+    compute_tile<D, NT>(W, B, lds.kst[wave], a, b, g, s, e_of(j + 1), e_end, lane, do_export, vec_export);
     load_tile<D>(B, a, b, s, e_of(j + 3), g, lane, slot_sm, e_begin, e_end);
   }
   if (j < nw) {
-    compute_tile<D, NT>(W, A, a, b, g, s, e_of(j), e_end, lane, do_export, vec_export);
+    compute_tile<D, NT>(W, A, lds.kst[wave], a, b, g, s, e_of(j), e_end, lane, do_export, vec_export);
     if (j + 2 < nw) load_tile<D>(A, a, b, s, e_of(j + 2), g, lane, slot_sm, e_begin, e_end);
   }
-  if (j + 1 < nw) compute_tile<D, NT>(W, B, a, b, g, s, e_of(j + 1), e_end, lane, do_export, vec_export);
-  if (j + 2 < nw) compute_tile<D, NT>(W, A, a, b, g, s, e_of(j + 2), e_end, lane, do_export, vec_export);
+  if (j + 1 < nw) compute_tile<D, NT>(W, B, lds.kst[wave], a, b, g, s, e_of(j + 1), e_end, lane, do_export, vec_export);
+  if (j + 2 < nw) compute_tile<D, NT>(W, A, lds.kst[wave], a, b, g, s, e_of(j + 2), e_end, lane, do_export, vec_export);
   }
 
+  __syncthreads();  // the K staging area becomes the merge area
   // Merge the 4 waves' states into this split's partial.
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {

@@ -19,9 +19,9 @@ using namespace vg;
 
 constexpr size_t kAlign = 256;
 #ifndef VG_TARGET_WGS
-#define VG_TARGET_WGS 512
+#define VG_TARGET_WGS 256
 #endif
-constexpr int kTargetWorkgroups = VG_TARGET_WGS;  // verify: two resident workgroups per CU on 256 CUs
+constexpr int kTargetWorkgroups = VG_TARGET_WGS;  // verify: one resident workgroup (4 waves, 2 tiles in flight each) per CU
 // Partial bytes per (b, g) up to which the last split workgroup combines in the
 // same launch.  0: the combine is always its own launch -- a workgroup-to-
 // workgroup handoff inside one launch needs a device-scope release, which on
@@ -113,7 +113,7 @@ float effective_scale(const vg_shape *s) {
 }
 
 #ifndef VG_VERIFY_PF
-#define VG_VERIFY_PF 1
+#define VG_VERIFY_PF 2
 #endif
 
 template <int D, int NT, bool FUSED>

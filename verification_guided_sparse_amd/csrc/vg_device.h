@@ -26,23 +26,48 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
 // Exponential in base 2 (hardware v_exp_f32).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lane l exchanges with lane l ^ 32 / l ^ 16 through v_permlane32_swap /
+// v_permlane16_swap: swapping a register with itself leaves {lower, upper}
+// halves (resp. {even, odd} 16-lane rows) in the two results, so combining
+// the two results gives the pairwise reduction in every lane.
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum / max across the 4 sixteen-lane groups (lanes l, l^16, l^32, l^48).
-__device__ __forceinline__ float sum_across_groups(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+__device__ __forceinline__ float sum_across_groups(float v) { return sum_xor32(sum_xor16(v)); }
+__device__ __forceinline__ float max_across_groups(float v) { return max_xor32(max_xor16(v)); }
+
+// DPP moves within a 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
-__device__ __forceinline__ float max_across_groups(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
-}
-// Sum across the 16 lanes of a group (lanes sharing l / 16).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// Sum across the 16 lanes of a group (lanes sharing l / 16): pairs, quads,
+// then the mirrored quad and the mirrored half-row.
 __device__ __forceinline__ float sum_within_group(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
+  v += dpp<kDppQuadXor1>(v);
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppRowHalfMirror>(v);
+  v += dpp<kDppRowMirror>(v);
   return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
