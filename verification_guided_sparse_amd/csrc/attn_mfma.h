@@ -81,14 +81,17 @@ struct KStage {
 //   sparse: the explicit slot list of the split (entries below cnt)
 constexpr int kSlotSm = 1024;
 
-__device__ __forceinline__ void stage_slots(int *slot_sm, const AttnArgs &a, int b, const SeqList &s,
-                                            int e_begin, int e_end) {
+// Issued before the sequence's lengths are known, so the window is the whole
+// split (clamped to the page-table row / slot list); entries past the
+// sequence are never read back.
+__device__ __forceinline__ void stage_slots(int *slot_sm, const AttnArgs &a, int b, int e_begin) {
   if (!a.sparse) {
-    const int p0 = e_begin >> 4, p1 = (e_end - 1) >> 4;
-    for (int i = threadIdx.x; i <= p1 - p0; i += kThreads)
+    const int p0 = e_begin >> 4;
+    const int n = min(a.split_tokens / kPageSize + 1, a.max_pages - p0);
+    for (int i = threadIdx.x; i < n; i += kThreads)
       slot_sm[i] = a.page_table[(size_t)b * a.max_pages + p0 + i];
   } else {
-    const int n = min(e_end, s.cnt) - e_begin;
+    const int n = min(a.split_tokens, a.max_k - e_begin);
     for (int i = threadIdx.x; i < n; i += kThreads)
       slot_sm[i] = a.sel_slot[(size_t)b * a.max_k + e_begin + i];
   }
@@ -300,9 +303,8 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
 
 // PF = tiles in flight per wave: 1 (load, then compute; two waves per SIMD)
 // or 2 (the next tile loads while this one computes; one wave per SIMD).
-template <int D, int NT, bool FUSED, int PF>
-__global__ __launch_bounds__(kThreads, PF == 1 ? 2 : 1) void attn_mfma_kernel(AttnArgs a,
-                                                                             uint32_t *counters) {
+template <int D, int NT, int PF>
+__global__ __launch_bounds__(kThreads, PF == 1 ? 2 : 1) void attn_mfma_kernel(AttnArgs a) {
   constexpr int KS = D / 32;   // k-steps of the QK^T contraction
   constexpr int DPL = D / 16;  // d values per lane per V row, = number of PV tiles
   constexpr int ROWS = NT * 16;
@@ -312,18 +314,17 @@ __global__ __launch_bounds__(kThreads, PF == 1 ? 2 : 1) void attn_mfma_kernel(At
   } lds;
   MergeSmem<ROWS, D> &sm = lds.m;
   __shared__ int slot_sm[kSlotSm];
-  __shared__ int sm_flag;
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q4 = lane >> 4, i16 = lane & 15;
+  const int e_begin = split * a.split_tokens;
+  stage_slots(slot_sm, a, b, e_begin);
   const SeqList s = seq_list(a, b);
   const int ns = num_splits_for(a, s.len);
   if (split >= ns) return;
-  const int e_begin = split * a.split_tokens;
   const int e_end = min(s.len, e_begin + a.split_tokens);
   const int G = a.group_size, M = a.rows, Hq = a.num_q_heads;
-  stage_slots(slot_sm, a, b, s, e_begin, e_end);
 
   WaveState<D, NT> W;
 #pragma unroll
@@ -410,10 +411,6 @@ __global__ __launch_bounds__(kThreads, PF == 1 ? 2 : 1) void attn_mfma_kernel(At
   }
   __syncthreads();
   merge_o<ROWS, D>(sm, a.part_o + pidx * D, M);
-  if constexpr (FUSED) {
-    __syncthreads();  // the merge area becomes combine scratch
-    finish_split<D>(a, counters, b, g, ns, &sm_flag, &sm.o[0][0][0]);
-  }
 }
 
 }  // namespace vg

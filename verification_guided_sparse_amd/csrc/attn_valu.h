@@ -55,12 +55,11 @@ struct ValuSmem {
   };
 };
 
-template <typename T, int D, int MR, bool FUSED>
-__global__ __launch_bounds__(kThreads, 1) void attn_valu_kernel(AttnArgs a, uint32_t *counters) {
+template <typename T, int D, int MR>
+__global__ __launch_bounds__(kThreads, 1) void attn_valu_kernel(AttnArgs a) {
   constexpr int DV = D / kWave;  // output columns per lane
   constexpr int CH = Elem<T>::kPer16B;
   __shared__ ValuSmem<MR, D> sm;
-  __shared__ int sm_flag;
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -189,10 +188,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_valu_kernel(AttnArgs a, uint
     for (int k = 0; k < DV; ++k) sm.merge.o[wave][m][lane * DV + k] = o[m][k];
   __syncthreads();
   merge_o<MR, D>(sm.merge, a.part_o + pidx * D, M);
-  if constexpr (FUSED) {
-    __syncthreads();  // the merge area becomes combine scratch
-    finish_split<D>(a, counters, b, g, ns, &sm_flag, &sm.merge.o[0][0][0]);
-  }
 }
 
 }  // namespace vg

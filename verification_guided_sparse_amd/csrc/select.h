@@ -71,15 +71,24 @@ struct SelArgs {
   SelWs ws;
 };
 
+// Inclusive prefix sum across the 64 lanes of a wave with DPP: shifts by
+// 1, 2, 4, 8 inside each 16-lane row (lanes without a source read 0), then the
+// last lane of row 0 (resp. of row 1) is broadcast into rows 1 and 3 (resp.
+// rows 2 and 3).
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
 // Exclusive prefix sum over a 256-thread block; `total` receives the sum.
 __device__ __forceinline__ int block_exclusive_scan(int v, int *sm4, int &total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_inclusive_scan(v);
   if (lane == 63) sm4[w] = x;
   __syncthreads();
   int pre = 0;
@@ -150,23 +159,39 @@ __global__ __launch_bounds__(kSelThreads) void select_pass1_kernel(SelArgs a) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) sc[i] = 0.f;
     const bool vec = ((a.max_prefix & 3) == 0) && (j0 + kPerThread <= P);
-    for (int r = 0; r < a.src_rows; ++r)
-      for (int h = 0; h < a.src_heads; ++h) {
-        const float *row = a.src + ((size_t)(b * a.src_rows + r) * a.src_heads + h) * a.max_prefix;
-        if (vec) {
-          const f32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + j0));
-          const f32x4 v1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + j0 + 4));
+    // rows (t, h) of src in order; batches of 8 rows whose loads are in flight together
+    const int nrow = a.src_rows * a.src_heads;
+    const float *base = a.src + (size_t)b * nrow * a.max_prefix;
+    if (vec) {
+      constexpr int U = 8;
+      for (int r0 = 0; r0 < nrow; r0 += U) {
+        f32x4 v[U][2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (r0 + u < nrow) {
+            const float *row = base + (size_t)(r0 + u) * a.max_prefix + j0;
+            v[u][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row));
+            v[u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 4));
+          } else {
+            v[u][0] = v[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            sc[i] += v0[i];
-            sc[4 + i] += v1[i];
+            sc[i] += v[u][0][i];
+            sc[4 + i] += v[u][1][i];
           }
-        } else {
-#pragma unroll
-          for (int i = 0; i < kPerThread; ++i)
-            if (j0 + i < P) sc[i] += row[j0 + i];
-        }
       }
+    } else {
+      for (int r = 0; r < nrow; ++r) {
+        const float *row = base + (size_t)r * a.max_prefix;
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i)
+          if (j0 + i < P) sc[i] += row[j0 + i];
+      }
+    }
     float *dst = a.scores_out + (size_t)b * a.max_prefix;
     if (vec) {
       *reinterpret_cast<f32x4 *>(dst + j0) = f32x4{sc[0], sc[1], sc[2], sc[3]};
@@ -221,6 +246,11 @@ __global__ __launch_bounds__(kSelThreads) void select_pass2_kernel(SelArgs a) {
   const int k_eff = min(a.k[b], P);
   const int nch = (P + kChunk - 1) / kChunk;
   if (w >= nch) return;
+  const int j0 = w * kChunk + t * kPerThread;
+  const float *srow = a.scores + (size_t)b * a.max_prefix;
+  float sv[kPerThread];  // issued before the histogram work so the loads overlap it
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) sv[i] = (j0 + i < P) ? srow[j0 + i] : 0.f;
   uint32_t b1 = 0xffffffffu;  // k_eff == 0: nothing above, no candidates
   int above1 = 0;
   if (k_eff > 0) b1 = load_hist_find_b1(a.ws.hist1 + (size_t)b * kBins1, lh, k_eff, sm4, sm_res, above1);
@@ -230,13 +260,11 @@ __global__ __launch_bounds__(kSelThreads) void select_pass2_kernel(SelArgs a) {
   }
   for (int i = t; i < kBins23; i += kSelThreads) lh[i] = 0u;  // candidates' bits [10,20)
   __syncthreads();
-  const int j0 = w * kChunk + t * kPerThread;
-  const float *srow = a.scores + (size_t)b * a.max_prefix;
   uint32_t key[kPerThread];
   int n_above = 0, n_cand = 0;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
-    key[i] = (j0 + i < P) ? score_key(srow[j0 + i]) : 0u;
+    key[i] = (j0 + i < P) ? score_key(sv[i]) : 0u;
     const bool in = (j0 + i < P) && (k_eff > 0);
     n_above += in && ((key[i] >> 20) > b1);
     const bool cand = in && ((key[i] >> 20) == b1);
@@ -277,6 +305,11 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
     return;
   }
   if (w >= nch) return;
+  const int j0 = w * kChunk + t * kPerThread;
+  const float *srow = a.scores + (size_t)b * a.max_prefix;
+  float sv[kPerThread];  // issued first: independent of everything below
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) sv[i] = (j0 + i < P) ? srow[j0 + i] : 0.f;
   if (w == 0) {  // every reader of hist1 has finished (pass 2): clear it for the next call
     u32x4 *g4 = reinterpret_cast<u32x4 *>(a.ws.hist1 + (size_t)b * kBins1) + 4 * t;
 #pragma unroll
@@ -413,13 +446,11 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
     __syncthreads();
   }
   // Select this chunk's entries in position order.
-  const int j0 = w * kChunk + t * kPerThread;
-  const float *srow = a.scores + (size_t)b * a.max_prefix;
   uint32_t key[kPerThread];
   int n_eq = 0;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
-    key[i] = (j0 + i < P) ? score_key(srow[j0 + i]) : 0u;
+    key[i] = (j0 + i < P) ? score_key(sv[i]) : 0u;
     n_eq += (j0 + i < P) && (key[i] == kstar);
   }
   int tot_eq;

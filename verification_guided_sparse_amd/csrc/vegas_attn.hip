@@ -23,13 +23,11 @@ constexpr size_t kAlign = 256;
 #endif
 constexpr int kTargetWorkgroups = VG_TARGET_WGS;  // verify: one resident workgroup (4 waves, 2 tiles in flight each) per CU
 // Partial bytes per (b, g) up to which the last split workgroup combines in the
-// same launch.  0: the combine is always its own launch -- a workgroup-to-
-// workgroup handoff inside one launch needs a device-scope release, which on
-// gfx950 writes back the whole L2 from every workgroup.
-#ifndef VG_FUSED_COMBINE_BYTES
-#define VG_FUSED_COMBINE_BYTES 0
+// same launch (one workgroup reads them all, so only small ones); larger ones
+// get a combine launch with one workgroup per output row.
+#ifndef VG_SPARSE_SPLIT
+#define VG_SPARSE_SPLIT 128  // minimum sparse split length (MFMA path)
 #endif
-constexpr size_t kFusedCombineBytes = VG_FUSED_COMBINE_BYTES;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -67,8 +65,8 @@ bool use_mfma(const vg_shape *s) {
 // Launch plan and workspace layout of one attention call.
 struct AttnPlan {
   int rows, nt, mr, splits, split_tokens;
-  bool mfma, fused, ok;  // ok: the key list fits kMaxSplits splits
-  size_t off_part_o, off_part_ml, off_counters, bytes;
+  bool mfma, ok;  // ok: the key list fits kMaxSplits splits
+  size_t off_part_o, off_part_ml, bytes;
 };
 
 AttnPlan plan_attention(const vg_shape *s, int nrows, long long max_len, bool sparse) {
@@ -84,6 +82,7 @@ AttnPlan plan_attention(const vg_shape *s, int nrows, long long max_len, bool sp
   if (sparse) {
     const long long mult = (len * bg) / ((long long)unit * 2048);
     p.split_tokens = unit * (int)(mult > 1 ? mult : 1);
+    if (p.mfma && p.split_tokens < VG_SPARSE_SPLIT) p.split_tokens = VG_SPARSE_SPLIT;
   } else {
     const long long per = (kTargetWorkgroups + bg - 1) / bg;
     long long st = (len + per - 1) / per;
@@ -100,11 +99,9 @@ AttnPlan plan_attention(const vg_shape *s, int nrows, long long max_len, bool sp
   p.splits = ceil_div(len, p.split_tokens);
   p.ok = p.splits <= kMaxSplits;
   const size_t n_part = (size_t)bg * p.splits * p.rows;
-  p.fused = kFusedCombineBytes > 0 && (size_t)p.splits * p.rows * s->head_dim * 4 <= kFusedCombineBytes;
   p.off_part_o = 0;
   p.off_part_ml = align_up(n_part * s->head_dim * sizeof(float));
-  p.off_counters = p.off_part_ml + align_up(n_part * 2 * sizeof(float));
-  p.bytes = p.off_counters + align_up((size_t)bg * sizeof(uint32_t));
+  p.bytes = p.off_part_ml + align_up(n_part * 2 * sizeof(float));
   return p;
 }
 
@@ -115,68 +112,61 @@ float effective_scale(const vg_shape *s) {
 #ifndef VG_VERIFY_PF
 #define VG_VERIFY_PF 2
 #endif
+#ifndef VG_SPARSE_PF
+#define VG_SPARSE_PF 1
+#endif
 
-template <int D, int NT, bool FUSED>
-void launch_mfma_nt(const AttnArgs &a, uint32_t *ctr, dim3 grid, hipStream_t st) {
-  if (a.sparse)  // one tile per wave: no pipelining, two waves per SIMD
-    hipLaunchKernelGGL((attn_mfma_kernel<D, NT, FUSED, 1>), grid, dim3(kThreads), 0, st, a, ctr);
+template <int D, int NT>
+void launch_mfma_nt(const AttnArgs &a, dim3 grid, hipStream_t st) {
+  if (a.sparse)
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NT, VG_SPARSE_PF>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<D, NT, FUSED, VG_VERIFY_PF>), grid, dim3(kThreads), 0, st, a, ctr);
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NT, VG_VERIFY_PF>), grid, dim3(kThreads), 0, st, a);
 }
 
-template <int D, bool FUSED>
-void launch_mfma_d(int nt, const AttnArgs &a, uint32_t *ctr, dim3 grid, hipStream_t st) {
+template <int D>
+void launch_mfma_d(int nt, const AttnArgs &a, dim3 grid, hipStream_t st) {
   switch (nt) {
-    case 1: launch_mfma_nt<D, 1, FUSED>(a, ctr, grid, st); break;
-    case 2: launch_mfma_nt<D, 2, FUSED>(a, ctr, grid, st); break;
-    case 3: launch_mfma_nt<D, 3, FUSED>(a, ctr, grid, st); break;
-    default: launch_mfma_nt<D, 4, FUSED>(a, ctr, grid, st); break;
+    case 1: launch_mfma_nt<D, 1>(a, grid, st); break;
+    case 2: launch_mfma_nt<D, 2>(a, grid, st); break;
+    case 3: launch_mfma_nt<D, 3>(a, grid, st); break;
+    default: launch_mfma_nt<D, 4>(a, grid, st); break;
   }
 }
 
-template <typename T, int D, bool FUSED>
-void launch_valu_t(int mr, const AttnArgs &a, uint32_t *ctr, dim3 grid, hipStream_t st) {
+template <typename T, int D>
+void launch_valu_t(int mr, const AttnArgs &a, dim3 grid, hipStream_t st) {
   switch (mr) {
-    case 16: hipLaunchKernelGGL((attn_valu_kernel<T, D, 16, FUSED>), grid, dim3(kThreads), 0, st, a, ctr); break;
-    case 32: hipLaunchKernelGGL((attn_valu_kernel<T, D, 32, FUSED>), grid, dim3(kThreads), 0, st, a, ctr); break;
-    default: hipLaunchKernelGGL((attn_valu_kernel<T, D, 64, FUSED>), grid, dim3(kThreads), 0, st, a, ctr); break;
+    case 16: hipLaunchKernelGGL((attn_valu_kernel<T, D, 16>), grid, dim3(kThreads), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((attn_valu_kernel<T, D, 32>), grid, dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((attn_valu_kernel<T, D, 64>), grid, dim3(kThreads), 0, st, a); break;
   }
 }
 
-template <bool FUSED>
-void launch_attn_fused(const vg_shape *s, const AttnPlan &p, const AttnArgs &a, uint32_t *ctr,
-                       hipStream_t st) {
-  const dim3 grid(p.splits, s->num_kv_heads, s->batch);
-  if (p.mfma) {
-    if (s->head_dim == 128) launch_mfma_d<128, FUSED>(p.nt, a, ctr, grid, st);
-    else launch_mfma_d<64, FUSED>(p.nt, a, ctr, grid, st);
-  } else if (s->dtype == VG_DTYPE_BF16) {
-    if (s->head_dim == 128) launch_valu_t<uint16_t, 128, FUSED>(p.mr, a, ctr, grid, st);
-    else launch_valu_t<uint16_t, 64, FUSED>(p.mr, a, ctr, grid, st);
-  } else {
-    if (s->head_dim == 128) launch_valu_t<float, 128, FUSED>(p.mr, a, ctr, grid, st);
-    else launch_valu_t<float, 64, FUSED>(p.mr, a, ctr, grid, st);
-  }
-}
-
+// Split kernel, then one combine block per (row, KV head, sequence).
 vg_status launch_attention(const vg_shape *s, const AttnPlan &p, AttnArgs &a, char *ws,
                            hipStream_t st) {
   a.part_o = reinterpret_cast<float *>(ws + p.off_part_o);
   a.part_ml = reinterpret_cast<float *>(ws + p.off_part_ml);
-  uint32_t *ctr = reinterpret_cast<uint32_t *>(ws + p.off_counters);
   a.splits = p.splits;
   a.split_tokens = p.split_tokens;
   a.rows = p.rows;
-  if (p.fused) {
-    launch_attn_fused<true>(s, p, a, ctr, st);
+  const dim3 grid(p.splits, s->num_kv_heads, s->batch);
+  if (p.mfma) {
+    if (s->head_dim == 128) launch_mfma_d<128>(p.nt, a, grid, st);
+    else launch_mfma_d<64>(p.nt, a, grid, st);
+  } else if (s->dtype == VG_DTYPE_BF16) {
+    if (s->head_dim == 128) launch_valu_t<uint16_t, 128>(p.mr, a, grid, st);
+    else launch_valu_t<uint16_t, 64>(p.mr, a, grid, st);
   } else {
-    launch_attn_fused<false>(s, p, a, ctr, st);
-    const dim3 cgrid(p.rows, s->num_kv_heads, s->batch);
-    if (s->head_dim == 128)
-      hipLaunchKernelGGL((combine_kernel<128>), cgrid, dim3(kThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL((combine_kernel<64>), cgrid, dim3(kThreads), 0, st, a);
+    if (s->head_dim == 128) launch_valu_t<float, 128>(p.mr, a, grid, st);
+    else launch_valu_t<float, 64>(p.mr, a, grid, st);
   }
+  const dim3 cgrid(p.rows, s->num_kv_heads, s->batch);
+  if (s->head_dim == 128)
+    hipLaunchKernelGGL((combine_kernel<128>), cgrid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<64>), cgrid, dim3(kThreads), 0, st, a);
   return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
 }
 
