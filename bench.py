@@ -108,7 +108,12 @@ def main():
     ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every step separately")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (HBM byte-counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs the path on a single MI355X; "
@@ -237,6 +242,18 @@ def main():
                       f"{c.gamma} draft steps) in fp64, {t:.2f} s",
         }
     print(json.dumps(result), flush=True)
+
+
+def calibrate_copy(nbytes):
+    """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE
+    counters scale the counters read for the attention kernels."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "launches": 3}), flush=True)
 
 
 def capture(fn):
