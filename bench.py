@@ -132,7 +132,7 @@ def main():
     layer_kv = int((c.prefix_len.astype(np.int64) + c.rows).sum()) * c.num_kv_heads * c.head_dim * 2 * (
         2 if c.dtype == "bf16" else 4)
     L = args.layers or max(2, int(np.ceil(3 * 256e6 / max(sum(ab["draft"]) / max(c.gamma, 1), 1))))
-    L = min(L, max(2, int(40e9 // layer_kv)))
+    L = min(L, 64, max(2, int(40e9 // layer_kv)))
     print(f"[bench] {args.workload}: {L} layers, {layer_kv / 1e6:.1f} MB KV per layer, "
           f"export={args.export}, kernel={args.kernel}", file=sys.stderr, flush=True)
 

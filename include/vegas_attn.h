@@ -69,7 +69,8 @@ typedef int32_t vg_status;
 
 /* Shape of one attention layer and its paged cache. */
 typedef struct vg_shape {
-  int32_t batch;             /* B >= 1 sequences */
+  int32_t batch;             /* B >= 1 sequences; attention calls take B <= 1024
+                                (more gives VG_ERR_UNSUPPORTED) */
   int32_t num_q_heads;       /* Hq, a multiple of num_kv_heads */
   int32_t num_kv_heads;      /* Hkv >= 1 */
   int32_t head_dim;          /* D: 64 or 128 */

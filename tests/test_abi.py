@@ -116,9 +116,16 @@ def test_topk_and_sparse_reject_before_launch():
     assert e.value.status == vg.VG_ERR_INVALID_ARG
 
 
-def test_oversized_key_lists_rejected():
-    """More keys than the split bookkeeping can hold is reported, not truncated."""
+def test_batch_limit_and_long_lists():
+    """Batches above the work-sharing table's capacity (1024 sequences) are
+    reported before any launch; long key lists are accepted (the workgroups
+    share tiles, so list length sets no limit)."""
+    sh = _shape(batch=1025, max_pages_per_seq=1 << 20)
+    for call in (lambda: vg.vg_sparse_draft_workspace_size(sh, 1, 100, 8),
+                 lambda: vg.vg_verify_workspace_size(sh, 4096, 3)):
+        with pytest.raises(vg.VgError) as e:
+            call()
+        assert e.value.status == vg.VG_ERR_UNSUPPORTED
     sh = _shape(max_pages_per_seq=1 << 20)
-    with pytest.raises(vg.VgError) as e:
-        vg.vg_sparse_draft_workspace_size(sh, 1, 600_000, 8)
-    assert e.value.status == vg.VG_ERR_UNSUPPORTED
+    assert vg.vg_sparse_draft_workspace_size(sh, 1, 600_000, 8) > 0
+    assert vg.vg_verify_workspace_size(sh, 1 << 21, 7) > 0

@@ -50,14 +50,14 @@ def _check(ok_msg, what):
     assert ok, f"{what}: {msg}"
 
 
-def _run_steps(c, kernel=None):
+def _run_steps(c, kernel=None, pad=64):
     """Per-step parity of one case; returns the device case for further checks."""
     from verification_guided_sparse_amd import _binding as vg
     from verification_guided_sparse_amd.runner import DeviceCase
     import torch
     _say(f"[parity] {c.cfg.name} B={c.batch} P={list(c.prefix_len)} Hq={c.num_q_heads} "
-         f"Hkv={c.num_kv_heads} D={c.head_dim} {c.dtype} gamma={c.gamma} kernel={kernel}")
-    dc = DeviceCase(c, kernel=vg.VG_KERNEL_AUTO if kernel is None else kernel)
+         f"Hkv={c.num_kv_heads} D={c.head_dim} {c.dtype} gamma={c.gamma} kernel={kernel} pad={pad}")
+    dc = DeviceCase(c, kernel=vg.VG_KERNEL_AUTO if kernel is None else kernel, pad=pad)
     out_ref, logits_ref, group_ref = _oracle_all(c)
 
     # verify + export (both forms)
@@ -70,10 +70,8 @@ def _run_steps(c, kernel=None):
            "verify group scores")
 
     # aggregate on the oracle's logits (fp32-rounded), both sources
-    lg32 = torch.from_numpy(logits_ref.astype(np.float32)).cuda()
-    gr32 = torch.from_numpy(group_ref.astype(np.float32)).cuda()
-    dc.logits.copy_(lg32)
-    dc.group.copy_(gr32)
+    dc.put("logits", logits_ref.astype(np.float32))
+    dc.put("group", group_ref.astype(np.float32))
     mask_s = _rows_mask(c, ())
     for src, ref_src in (("raw", logits_ref.astype(np.float32)), ("group", group_ref.astype(np.float32))):
         dc.aggregate(src=src)
@@ -85,7 +83,7 @@ def _run_steps(c, kernel=None):
     # taking the same decision in the same precision
     s_ref = oracle.aggregate(logits_ref, c.prefix_len)
     s32 = s_ref.astype(np.float32)
-    dc.scores.copy_(torch.from_numpy(s32).cuda())
+    dc.put("scores", s32)
     dc.topk()
     torch.cuda.synchronize()
     pos_ref, slot_ref, cnt_ref = oracle.topk(s32.astype(np.float64), c.prefix_len, c.k,
@@ -155,6 +153,15 @@ SMALL = {
 def test_small_parity(torch_cuda, name):
     c = synth.make_case(SMALL[name]())
     dc, refs = _run_steps(c)
+    _run_chain(c, dc, refs, "group")
+    _run_chain(c, dc, refs, "raw")
+
+
+@pytest.mark.parametrize("name", ["c4_small", "c5_small", "short_prefixes"])
+def test_small_parity_unpadded_rows(torch_cuda, name):
+    """Export / score rows exactly max_prefix floats long (unaligned strides)."""
+    c = synth.make_case(SMALL[name]())
+    dc, refs = _run_steps(c, pad=1)
     _run_chain(c, dc, refs, "group")
     _run_chain(c, dc, refs, "raw")
 

@@ -1,10 +1,10 @@
-// attn_common.h -- split-KV bookkeeping shared by the MFMA and VALU attention
-// kernels: the per-workgroup merge of its waves' online-softmax states, the
-// per-split partial results, and the combine of the splits of one
-// (sequence, KV head).
+// attn_common.h -- work sharing bookkeeping of the MFMA and VALU attention
+// kernels: the walk over a workgroup's share of the key tiles, the merge of its
+// waves' online-softmax states into one partial result per piece, and the
+// combine of the partials of one (sequence, KV head).
 //
-// Every merge sums in a fixed order (wave 0..3, split 0..S-1), so results do
-// not depend on which workgroup finishes first.
+// Every merge sums in a fixed order (wave 0..3, workgroups in index order), so
+// results do not depend on which workgroup finishes first.
 #pragma once
 
 #include "vg_device.h"
@@ -26,7 +26,7 @@ struct MergeSmem {
 
 // Step 1: each wave has written m[w][row] (log2 domain) and l[w][row] (full row
 // sums).  Computes the per-wave weights f = exp2(m_w - max_w m_w) and writes
-// this split's (m, l) for rows < M to part_ml.  Call between barriers.
+// this piece's (m, l) for rows < M to part_ml.  Call between barriers.
 template <int ROWS, int D>
 __device__ __forceinline__ void merge_stats(MergeSmem<ROWS, D> &sm, float *part_ml, int M) {
   const int t = threadIdx.x;
@@ -65,48 +65,149 @@ __device__ __forceinline__ void merge_o(MergeSmem<ROWS, D> &sm, float *part_o, i
   }
 }
 
-__device__ __forceinline__ size_t part_index(const AttnArgs &a, int b, int g, int split) {
-  return ((size_t)(b * a.num_kv_heads + g) * a.splits + split) * a.rows;
+// ---- work split index math (host and device; the host build is tested) ----
+
+// Stream-K walk of workgroup w: tiles [t, t_end) remain, the next one in
+// sequence b.  pre[b] = tiles of sequences before b (pre[batch] = all).
+struct ShareWalk {
+  int t, t_end, b;
+};
+
+__host__ __device__ inline ShareWalk share_walk_begin(const int *pre, int batch, int Hkv, int w, int W) {
+  ShareWalk s;
+  const long long T = (long long)Hkv * pre[batch];
+  s.t = (int)share_begin(w, T, W);
+  s.t_end = (int)share_begin(w + 1, T, W);
+  // sequence holding tile t: largest b with Hkv * pre[b] <= t
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((long long)Hkv * pre[mid] <= s.t) lo = mid; else hi = mid - 1;
+  }
+  s.b = lo;
+  return s;
 }
 
-// Combining the splits of (b, g) for one output row:
-//   out = sum_s w_s O_s / sum_s w_s l_s,  w_s = exp2(m_s - max_s m_s).
-// One 256-thread block per row; thread (split group sg, float4 column col)
-// takes splits sg, sg + SP, ... in batches of kBatch whose (m, l, O) loads are
-// all in flight together, keeping an online (max, denominator, sum) state; the
-// groups' states are then merged through LDS.  One batch covers
-// kBatch * SP >= 64 splits, so a typical row costs one memory round trip.
-constexpr int kMaxSplits = 512;
+// A piece: entries [e_begin, e_end) of the list of sequence b, KV head g,
+// whose partial result goes to index `part`.
+struct Piece {
+  int b, g, part, e_begin, e_end;
+};
 
+// Next piece of a stream-K walk (call while s.t < s.t_end); len[b] = list lengths.
+template <typename LenFn>
+__host__ __device__ inline Piece share_walk_next(ShareWalk &s, const int *pre, int Hkv, int tile, int w,
+                                                 LenFn len) {
+  int n = pre[s.b + 1] - pre[s.b];
+  while (n == 0) {  // lists without tiles (none for valid inputs)
+    ++s.b;
+    n = pre[s.b + 1] - pre[s.b];
+  }
+  const int sb = Hkv * pre[s.b];
+  Piece p;
+  p.b = s.b;
+  p.g = (s.t - sb) / n;
+  const int seg_start = sb + p.g * n;
+  const int hi_t = s.t_end < seg_start + n ? s.t_end : seg_start + n;
+  const int L = len(p.b);
+  p.e_begin = (s.t - seg_start) * tile;
+  p.e_end = (hi_t - seg_start) * tile;
+  if (p.e_end > L) p.e_end = L;
+  p.part = w + p.b * Hkv + p.g;
+  s.t = hi_t;
+  if (p.g == Hkv - 1 && s.t == seg_start + n) ++s.b;  // the next piece starts in the next sequence
+  return p;
+}
+
+// The piece of workgroup w with fixed splits (empty past the list's end).
+__host__ __device__ inline Piece fixed_piece(int w, int splits, int split_tokens, int Hkv, int list_len) {
+  Piece p;
+  const int seg = w / splits, sp = w % splits;
+  p.b = seg / Hkv;
+  p.g = seg % Hkv;
+  p.part = w;
+  const long long e0 = (long long)sp * split_tokens;
+  p.e_begin = (int)(e0 < list_len ? e0 : list_len);
+  p.e_end = (int)(e0 + split_tokens < list_len ? e0 + split_tokens : list_len);
+  return p;
+}
+
+// Partials of segment (b, g) for the combine: indices first + j, j < count.
+// With shared tiles, index first + j is only valid if workgroup w = first + j -
+// seg has a share that meets the segment (share_meets).
+__host__ __device__ inline void combine_range(const int *pre, int batch, int Hkv, int W, int b, int g,
+                                              int &first, int &count) {
+  const long long T = (long long)Hkv * pre[batch];
+  const int n = pre[b + 1] - pre[b];
+  const long long S = (long long)Hkv * pre[b] + (long long)g * n;  // segment's first tile
+  // workgroups whose share [share_begin(w), share_begin(w + 1)) meets [S, S + n)
+  int w_first = (int)(((S + 1) * W + T - 1) / T) - 1;
+  int w_last = (int)(((S + n) * W + T - 1) / T) - 1;
+  w_first = w_first < 0 ? 0 : (w_first > W - 1 ? W - 1 : w_first);
+  w_last = w_last > W - 1 ? W - 1 : w_last;
+  if (w_last < w_first) w_last = w_first;
+  first = w_first + b * Hkv + g;
+  count = w_last - w_first + 1;
+}
+
+__host__ __device__ inline bool share_meets(const int *pre, int batch, int Hkv, int W, int w, int b, int g) {
+  const long long T = (long long)Hkv * pre[batch];
+  const int n = pre[b + 1] - pre[b];
+  const long long S = (long long)Hkv * pre[b] + (long long)g * n;
+  const long long lo = share_begin(w, T, W), hi = share_begin(w + 1, T, W);
+  return (lo > S ? lo : S) < (hi < S + n ? hi : S + n);
+}
+
+// Combining the partials of segment (b, g) for one output row:
+//   out = sum_w c_w O_w / sum_w c_w l_w,  c_w = exp2(m_w - max_w m_w)
+// over the workgroups w whose share of the tiles meets the segment (or over
+// the segment's fixed splits).  One
+// 256-thread block per row; thread (group sg, float4 column col) takes
+// partials sg, sg + SP, ... in batches whose (m, l, O) loads are all in
+// flight together, keeping an online (max, denominator, sum) state; the
+// groups' states are then merged through LDS.
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
   constexpr int C = D / 4;          // float4 columns of a row
-  constexpr int SP = kThreads / C;  // split groups
+  constexpr int SP = kThreads / C;  // partial groups
   constexpr int kBatch = 8;
+  __shared__ int pre[kMaxBatch + 1];
+  __shared__ int sm4[4];
   __shared__ float sm_m[kThreads];
   __shared__ float sm_d[SP];
   __shared__ f32x4 sm_o[kThreads];
   const int row = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
-  const SeqList s = seq_list(a, b);
-  const int ns = num_splits_for(a, s.len);
-  const int M = a.rows, G = a.group_size;
+  const int Hkv = a.num_kv_heads, W = a.workgroups;
+  const bool fixed = a.split_tokens > 0;
+  int first, np;
+  if (fixed) {  // partials seg * splits .. + splits - 1, all written
+    first = (b * Hkv + g) * a.splits;
+    np = a.splits;
+  } else {
+    load_tile_prefix(a, pre, sm4);
+    combine_range(pre, a.batch, Hkv, W, b, g, first, np);
+  }
+  const int seg = b * Hkv + g, M = a.rows, G = a.group_size;
   const int col = t % C, sg = t / C;
-  const float *pml = a.part_ml + (part_index(a, b, g, 0) + row) * 2;
-  const float *po = a.part_o + (part_index(a, b, g, 0) + row) * D + 4 * col;
+  const size_t p0 = (size_t)first * M + row;  // partial j lives at p0 + j * M
+  const float *pml = a.part_ml + p0 * 2;
+  const float *po = a.part_o + p0 * D + 4 * col;
   const size_t ml_stride = (size_t)M * 2, o_stride = (size_t)M * D;
 
   float mt = kMInit, dt = 0.f;
   f32x4 at = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = sg; s0 < ns; s0 += kBatch * SP) {
+  for (int j0 = sg; j0 < np; j0 += kBatch * SP) {
     float m[kBatch], l[kBatch];
     f32x4 o[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      const int sp = s0 + i * SP;
-      const bool ok = sp < ns;
-      m[i] = ok ? pml[sp * ml_stride] : kMInit;
-      l[i] = ok ? pml[sp * ml_stride + 1] : 0.f;
-      o[i] = ok ? *reinterpret_cast<const f32x4 *>(po + sp * o_stride) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const int j = j0 + i * SP;
+      bool ok = j < np;
+      // the workgroup's share may miss the segment (more workgroups than tiles)
+      if (ok && !fixed) ok = share_meets(pre, a.batch, Hkv, W, first + j - seg, b, g);
+      m[i] = ok ? pml[j * ml_stride] : kMInit;
+      l[i] = ok ? pml[j * ml_stride + 1] : 0.f;
+      o[i] = ok ? *reinterpret_cast<const f32x4 *>(po + j * o_stride) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float mb = mt;
 #pragma unroll
@@ -122,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
     }
     mt = mb;
   }
-  // merge the split groups: max, then rescaled sums
+  // merge the groups: max, then rescaled sums
   sm_m[t] = mt;
   __syncthreads();
   float mx = kMInit;
@@ -141,6 +242,42 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
     const int qr = row / G, h = g * G + row % G;
     *reinterpret_cast<f32x4 *>(a.out + (((size_t)b * a.nrows + qr) * a.num_q_heads + h) * D + 4 * t) =
         acc * (1.0f / den);
+  }
+}
+
+// Calls fn(b, g, part, e_begin, e_end) for each piece of this workgroup's work
+// (uniform across the block): entries [e_begin, e_end) of the list of segment
+// (b, g), whose partial result goes to index `part`.  With fixed splits a
+// workgroup past its list's end gets one empty piece (e_begin == e_end).
+// pre / sm4: LDS for load_tile_prefix.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Calls fn(b, g, part, e_begin, e_end) for each piece of this workgroup's work
+// (uniform across the block).  With fixed splits a workgroup past its list's
+// end gets one empty piece (e_begin == e_end).  pre / sm4: LDS for
+// load_tile_prefix.
+template <typename Fn>
+__device__ __forceinline__ void for_each_piece(const AttnArgs &a, int *pre, int *sm4, Fn fn) {
+  const int W = a.workgroups, w = blockIdx.x, Hkv = a.num_kv_heads;
+  const bool fixed = a.split_tokens > 0;
+  ShareWalk s{0, 1, 0};
+  if (!fixed) {
+    load_tile_prefix(a, pre, sm4);
+    s = share_walk_begin(pre, a.batch, Hkv, w, W);
+  }
+  auto len = [&](int b) { return seq_list(a, b).len; };
+  // One call site for fn, so that it is inlined once.
+  while (s.t < s.t_end) {
+    Piece p;
+    if (fixed) {
+      const int b = w / a.splits / Hkv;
+      p = fixed_piece(w, a.splits, a.split_tokens, Hkv, len(b));
+      s.t = s.t_end;
+    } else {
+      p = share_walk_next(s, pre, Hkv, a.tile, w, len);
+    }
+    // wave-uniform values: scalar registers
+    fn(uniform(p.b), uniform(p.g), uniform(p.part), uniform(p.e_begin), uniform(p.e_end));
   }
 }
 

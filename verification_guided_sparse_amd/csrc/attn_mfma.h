@@ -1,12 +1,14 @@
-// attn_mfma.h -- bf16 split-KV attention on the CDNA4 matrix cores
+// attn_mfma.h -- bf16 attention over paged key lists on the CDNA4 matrix cores
 // (v_mfma_f32_16x16x32_bf16), used for both verification attention (all
 // cache positions, causal among the new rows, logit export) and sparse draft
 // attention (selected slots + causal tail).
 //
-// One workgroup = 4 waves = one (split, KV head g, sequence b).  The query
-// rows of KV head g (M = nrows * G, padded to NT tiles of 16) stay in
-// registers for the whole split.  Each wave walks 32-entry tiles of the
-// split's key list (tiles t = wave, wave + 4, ...):
+// The 32-entry tiles of all (sequence b, KV head g) key lists are shared
+// evenly among the workgroups (attn_common.h); a workgroup = 4 waves walks its
+// share piece by piece, a piece being the part of the share inside one list.
+// For a piece the query rows of KV head g (M = nrows * G, padded to NT tiles of
+// 16) stay in registers; each wave takes the piece's tiles t = wave, wave + 4,
+// ...:
 //
 //   S^T[tok][row] = K[tok][:] . Q[row][:]     A = K rows straight from HBM,
 //                                             B = Q^T held in registers
@@ -75,27 +77,29 @@ struct KStage {
   char rows[32 * kRowBytes];
 };
 
-// Slots of a split's entries, staged in LDS once per workgroup so that the
-// tile loop issues its K/V loads without a dependent page-table load first.
-//   verify: page ids of the split's pages (entry e -> slot_sm[e/16 - page0] * 16 + e % 16)
-//   sparse: the explicit slot list of the split (entries below cnt)
+// Slots of a chunk of a piece's entries, staged in LDS once per workgroup so
+// that the tile loop issues its K/V loads without a dependent page-table load.
+//   verify: page ids of the chunk's pages (entry e -> slot_sm[e/16 - page0] * 16 + e % 16)
+//   sparse: the chunk's part of the explicit slot list (entries below cnt)
 constexpr int kSlotSm = 1024;
 
-// Issued before the sequence's lengths are known, so the window is the whole
-// split (clamped to the page-table row / slot list); entries past the
-// sequence are never read back.
-__device__ __forceinline__ void stage_slots(int *slot_sm, const AttnArgs &a, int b, int e_begin) {
+__device__ __forceinline__ void stage_slots(int *slot_sm, const AttnArgs &a, int b, const SeqList &s,
+                                            int e_begin, int e_end) {
   if (!a.sparse) {
-    const int p0 = e_begin >> 4;
-    const int n = min(a.split_tokens / kPageSize + 1, a.max_pages - p0);
+    const int p0 = e_begin >> 4, n = ((e_end - 1) >> 4) - p0 + 1;
     for (int i = threadIdx.x; i < n; i += kThreads)
       slot_sm[i] = a.page_table[(size_t)b * a.max_pages + p0 + i];
   } else {
-    const int n = min(a.split_tokens, a.max_k - e_begin);
+    const int n = min(e_end, s.cnt) - e_begin;
     for (int i = threadIdx.x; i < n; i += kThreads)
       slot_sm[i] = a.sel_slot[(size_t)b * a.max_k + e_begin + i];
   }
 }
+
+// Entries staged per chunk of a piece: verify stages page ids (1 per 16
+// entries), sparse stages slots (1 per entry).
+constexpr int kVerifyChunk = 512 * kPageSize;
+constexpr int kSparseChunk = kSlotSm;
 
 __device__ __forceinline__ int staged_slot(const int *slot_sm, const AttnArgs &a, int b,
                                            const SeqList &s, int e_begin, int e) {
@@ -113,7 +117,7 @@ __device__ __forceinline__ void load_tile(KVTile<D> &T, const AttnArgs &a, int b
   const size_t slot_bytes = (size_t)a.num_kv_heads * D * 2;
   const size_t head_off = (size_t)g * D * 2;
   // slot of entry e0 + (lane & 31); each lane then picks the slots it loads.
-  // Entries past the split's end (masked later) reuse its last entry, whose
+  // Entries past the chunk's end (masked later) reuse its last entry, whose
   // slot is staged.
   const int my_e = min(e0 + (lane & 31), e_end - 1);
   const int my_slot = staged_slot(slot_sm, a, b, s, e_begin, my_e);
@@ -144,6 +148,11 @@ struct WaveState {
   u32x4 qf[NT][D / 32];  // Q^T fragments (B operand of S^T = K Q^T)
   f32x4 o[NT][D / 16];   // O^T accumulators
   float m_run[NT], l_run[NT];
+  // per-lane constants of this lane's rows (row = rt*16 + i16)
+  int vis_off[NT];       // the row sees entries i < s.vis0 + vis_off
+  int head[NT];          // its query head, -1 for padding rows
+  float gw[NT];          // weight of the row in the group export: #{r in {0, gamma}}
+  int xrow[NT];          // export slots: bit 0 -> row 0 of the export, bit 1 -> row gamma
 };
 
 template <int D, int NT>
@@ -154,7 +163,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
   constexpr int KS = D / 32, DPL = D / 16;
   constexpr int CH = D / 8, RPI = 64 / CH, RB = KStage<D>::kRowBytes;
   const int q4 = lane >> 4, i16 = lane & 15;
-  const int G = a.group_size, M = a.rows, Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
 
   // K rows -> LDS -> operand layout (this wave's staging area only)
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -193,12 +202,11 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
     if (a.logits) {
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) {
-        const int row = rt * 16 + i16;
-        if (row < M) {
-          const int r = row / G, h = g * G + row % G;
+        if (W.xrow[rt]) {
+          const int h = W.head[rt];
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
-            if ((x == 0 && r == 0) || (x == 1 && r == a.gamma)) {
+            if (W.xrow[rt] & (1 << x)) {
               float *dst = a.logits + ((size_t)(b * 2 + x) * Hq + h) * a.max_prefix;
 #pragma unroll
               for (int tt = 0; tt < 2; ++tt) {
@@ -223,12 +231,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
       for (int tt = 0; tt < 2; ++tt) {
         f32x4 gs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rt = 0; rt < NT; ++rt) {
-          const int row = rt * 16 + i16;
-          const int r = row / G;
-          const float w = (row < M) ? (float)((r == 0) + (r == a.gamma)) : 0.f;
-          gs += w * st[tt][rt];
-        }
+        for (int rt = 0; rt < NT; ++rt) gs += W.gw[rt] * st[tt][rt];
 #pragma unroll
         for (int c = 0; c < 4; ++c) gs[c] = sum_within_group(gs[c]) * a.scale;
         if (i16 == 0) {
@@ -245,26 +248,42 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
     }
   }
 
-  // Online softmax (base 2) and P^T fragments.
+  // Online softmax (base 2) and P^T fragments.  Masking is only needed on
+  // tiles that reach past the chunk's end or into the causal part of the key
+  // list; O is rescaled only if some row's running maximum grew (otherwise
+  // every alpha is exactly 1).
+  const bool full = (e0 + 32 <= e_end) && (e0 + 32 <= s.vis0);
   bf16x8 pb[NT];
+  float alpha[NT];
+  bool grew = false;
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
-    const int row = rt * 16 + i16;
-    const int vis = s.vis0 + row / G;  // entries i < vis are visible to this row
     float x[2][4];
     float mx = kMInit;
+    if (full) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int e = e0 + tt * 16 + 4 * q4 + c;
-        const bool ok = (e < e_end) && (e < vis);
-        x[tt][c] = ok ? st[tt][rt][c] * a.scale_log2 : kNegInf;
-        mx = fmaxf(mx, x[tt][c]);
-      }
+        for (int c = 0; c < 4; ++c) {
+          x[tt][c] = st[tt][rt][c] * a.scale_log2;
+          mx = fmaxf(mx, x[tt][c]);
+        }
+    } else {
+      const int vis = s.vis0 + W.vis_off[rt];  // entries i < vis are visible to this row
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int e = e0 + tt * 16 + 4 * q4 + c;
+          const bool ok = (e < e_end) && (e < vis);
+          x[tt][c] = ok ? st[tt][rt][c] * a.scale_log2 : kNegInf;
+          mx = fmaxf(mx, x[tt][c]);
+        }
+    }
     mx = max_across_groups(mx);
     const float m_new = fmaxf(W.m_run[rt], mx);
-    const float alpha = exp2_fast(W.m_run[rt] - m_new);
+    grew |= m_new > W.m_run[rt];
+    alpha[rt] = exp2_fast(W.m_run[rt] - m_new);
     W.m_run[rt] = m_new;
     float p[2][4];
     float psum = 0.f;
@@ -275,15 +294,19 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
         p[tt][c] = exp2_fast(x[tt][c] - m_new);
         psum += p[tt][c];
       }
-    W.l_run[rt] = W.l_run[rt] * alpha + psum;
-#pragma unroll
-    for (int at = 0; at < DPL; ++at) W.o[rt][at] *= alpha;
+    W.l_run[rt] = W.l_run[rt] * alpha[rt] + psum;
     u32x4 pk;
     pk[0] = f32x2_to_bf16x2(p[0][0], p[0][1]);
     pk[1] = f32x2_to_bf16x2(p[0][2], p[0][3]);
     pk[2] = f32x2_to_bf16x2(p[1][0], p[1][1]);
     pk[3] = f32x2_to_bf16x2(p[1][2], p[1][3]);
     pb[rt] = as_bf16x8(pk);
+  }
+  if (__builtin_amdgcn_ballot_w64(grew)) {
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+      for (int at = 0; at < DPL; ++at) W.o[rt][at] *= alpha[rt];
   }
 
   // O^T += V^T P^T
@@ -301,10 +324,10 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
   }
 }
 
-// PF = tiles in flight per wave: 1 (load, then compute; two waves per SIMD)
-// or 2 (the next tile loads while this one computes; one wave per SIMD).
+// PF = tiles in flight per wave.  PF == 1: load, then compute, two waves per
+// SIMD; PF > 1: a ring of PF tiles, one wave per SIMD.
 template <int D, int NT, int PF>
-__global__ __launch_bounds__(kThreads, PF == 1 ? 2 : 1) void attn_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, (PF == 1 && NT <= 2) ? 2 : 1) void attn_mfma_kernel(AttnArgs a) {
   constexpr int KS = D / 32;   // k-steps of the QK^T contraction
   constexpr int DPL = D / 16;  // d values per lane per V row, = number of PV tiles
   constexpr int ROWS = NT * 16;
@@ -314,103 +337,110 @@ __global__ __launch_bounds__(kThreads, PF == 1 ? 2 : 1) void attn_mfma_kernel(At
   } lds;
   MergeSmem<ROWS, D> &sm = lds.m;
   __shared__ int slot_sm[kSlotSm];
+  __shared__ int pre[kMaxBatch + 1];
+  __shared__ int sm4[4];
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q4 = lane >> 4, i16 = lane & 15;
-  const int e_begin = split * a.split_tokens;
-  stage_slots(slot_sm, a, b, e_begin);
-  const SeqList s = seq_list(a, b);
-  const int ns = num_splits_for(a, s.len);
-  if (split >= ns) return;
-  const int e_end = min(s.len, e_begin + a.split_tokens);
   const int G = a.group_size, M = a.rows, Hq = a.num_q_heads;
-
-  WaveState<D, NT> W;
-#pragma unroll
-  for (int rt = 0; rt < NT; ++rt) {
-    const int row = rt * 16 + i16;
-    if (row < M) {
-      const int r = row / G, h = g * G + row % G;
-      const uint16_t *qrow =
-          static_cast<const uint16_t *>(a.q) + ((size_t)(b * a.nrows + r) * Hq + h) * D;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        W.qf[rt][ks] = *reinterpret_cast<const u32x4 *>(qrow + (4 * ks + q4) * 8);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) W.qf[rt][ks] = u32x4{0u, 0u, 0u, 0u};
-    }
-    W.m_run[rt] = kMInit;
-    W.l_run[rt] = 0.f;
-#pragma unroll
-    for (int at = 0; at < DPL; ++at) W.o[rt][at] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
   const bool do_export = !a.sparse && (a.logits != nullptr || a.group != nullptr);
   const bool vec_export = (a.max_prefix & 3) == 0;
-  __syncthreads();  // slot_sm ready
+  const int chunk = a.sparse ? kSparseChunk : kVerifyChunk;
 
-  // This wave's tiles: j = 0 .. nw-1 cover entries e_begin + 32 * (wave + 4 j).
-  const int ntiles = (e_end - e_begin + 31) / 32;
-  const int nw = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-  auto e_of = [&](int j) { return e_begin + 32 * (wave + kWaves * j); };
-  if constexpr (PF == 1) {
-    for (int j = 0; j < nw; ++j) {
-      KVTile<D> A;
-      load_tile<D>(A, a, b, s, e_of(j), g, lane, slot_sm, e_begin, e_end);
-      compute_tile<D, NT>(W, A, lds.kst[wave], a, b, g, s, e_of(j), e_end, lane, do_export, vec_export);
+  for_each_piece(a, pre, sm4, [&](int b, int g, int part, int e_begin, int e_end) {
+    const SeqList s = seq_list(a, b);
+    WaveState<D, NT> W;
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      const int row = rt * 16 + i16;
+      if (row < M) {
+        const int r = row / G, h = g * G + row % G;
+        const uint16_t *qrow =
+            static_cast<const uint16_t *>(a.q) + ((size_t)(b * a.nrows + r) * Hq + h) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          W.qf[rt][ks] = *reinterpret_cast<const u32x4 *>(qrow + (4 * ks + q4) * 8);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) W.qf[rt][ks] = u32x4{0u, 0u, 0u, 0u};
+      }
+      W.m_run[rt] = kMInit;
+      W.l_run[rt] = 0.f;
+      const int r = row / G;
+      W.vis_off[rt] = r;
+      W.head[rt] = row < M ? g * G + row % G : -1;
+      W.gw[rt] = row < M ? (float)((r == 0) + (r == a.gamma)) : 0.f;
+      W.xrow[rt] = row < M ? ((r == 0) | ((r == a.gamma) << 1)) : 0;
+#pragma unroll
+      for (int at = 0; at < DPL; ++at) W.o[rt][at] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  } else {
-  // Two tiles in flight: tile j+1 loads while tile j computes.  In the steady
-  // state every iteration issues its loads unconditionally, so the wait before
-  // a tile covers exactly that tile's (older) loads.
-  KVTile<D> A, B;
-  if (nw > 0) load_tile<D>(A, a, b, s, e_of(0), g, lane, slot_sm, e_begin, e_end);
-  if (nw > 1) load_tile<D>(B, a, b, s, e_of(1), g, lane, slot_sm, e_begin, e_end);
-  int j = 0;
-  for (; j + 3 < nw; j += 2) {
-    compute_tile<D, NT>(W, A, lds.kst[wave], a, b, g, s, e_of(j), e_end, lane, do_export, vec_export);
-    load_tile<D>(A, a, b, s, e_of(j + 2), g, lane, slot_sm, e_begin, e_end);
-    compute_tile<D, NT>(W, B, lds.kst[wave], a, b, g, s, e_of(j + 1), e_end, lane, do_export, vec_export);
-    load_tile<D>(B, a, b, s, e_of(j + 3), g, lane, slot_sm, e_begin, e_end);
-  }
-  if (j < nw) {
-    compute_tile<D, NT>(W, A, lds.kst[wave], a, b, g, s, e_of(j), e_end, lane, do_export, vec_export);
-    if (j + 2 < nw) load_tile<D>(A, a, b, s, e_of(j + 2), g, lane, slot_sm, e_begin, e_end);
-  }
-  if (j + 1 < nw) compute_tile<D, NT>(W, B, lds.kst[wave], a, b, g, s, e_of(j + 1), e_end, lane, do_export, vec_export);
-  if (j + 2 < nw) compute_tile<D, NT>(W, A, lds.kst[wave], a, b, g, s, e_of(j + 2), e_end, lane, do_export, vec_export);
-  }
 
-  __syncthreads();  // the K staging area becomes the merge area
-  // Merge the 4 waves' states into this split's partial.
+    for (int c0 = e_begin; c0 < e_end; c0 += chunk) {
+      const int c1 = min(e_end, c0 + chunk);
+      __syncthreads();  // earlier users of slot_sm / the K staging area are done
+      stage_slots(slot_sm, a, b, s, c0, c1);
+      __syncthreads();
+      // This wave's tiles: j = 0 .. nw-1 cover entries c0 + 32 * (wave + 4 j).
+      const int ntiles = (c1 - c0 + 31) / 32;
+      const int nw = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+      auto e_of = [&](int j) { return c0 + 32 * (wave + kWaves * j); };
+      // PF tiles in flight per wave: tile j + PF loads while tile j computes.
+      // In the steady state every load is issued unconditionally, so the wait
+      // before a tile covers exactly that tile's (oldest) loads.
+      KVTile<D> T[PF];
 #pragma unroll
-  for (int rt = 0; rt < NT; ++rt) {
-    const float lsum = sum_across_groups(W.l_run[rt]);
-    if (q4 == 0) {
-      sm.m[wave][rt * 16 + i16] = W.m_run[rt];
-      sm.l[wave][rt * 16 + i16] = lsum;
+      for (int u = 0; u < PF; ++u)
+        if (u < nw) load_tile<D>(T[u], a, b, s, e_of(u), g, lane, slot_sm, c0, c1);
+      int j = 0;
+      for (; j + 2 * PF <= nw; j += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          compute_tile<D, NT>(W, T[u], lds.kst[wave], a, b, g, s, e_of(j + u), c1, lane, do_export, vec_export);
+          load_tile<D>(T[u], a, b, s, e_of(j + u + PF), g, lane, slot_sm, c0, c1);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        if (j + u < nw) {
+          compute_tile<D, NT>(W, T[u], lds.kst[wave], a, b, g, s, e_of(j + u), c1, lane, do_export, vec_export);
+          if (j + u + PF < nw) load_tile<D>(T[u], a, b, s, e_of(j + u + PF), g, lane, slot_sm, c0, c1);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < PF; ++u)
+        if (j + PF + u < nw)
+          compute_tile<D, NT>(W, T[u], lds.kst[wave], a, b, g, s, e_of(j + PF + u), c1, lane, do_export, vec_export);
     }
-  }
-  __syncthreads();
-  const size_t pidx = part_index(a, b, g, split);
-  merge_stats<ROWS, D>(sm, a.part_ml + pidx * 2, M);
-  // O^T tile `at`, register c holds row (rt*16 + i16), d = DPL*(4*q4 + c) + at.
+
+    __syncthreads();  // the K staging area becomes the merge area
+    // Merge the 4 waves' states into this piece's partial.
 #pragma unroll
-  for (int rt = 0; rt < NT; ++rt) {
-    float *orow = &sm.o[wave][rt * 16 + i16][0];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int d0 = DPL * (4 * q4 + c);
-#pragma unroll
-      for (int at = 0; at < DPL; at += 4)
-        *reinterpret_cast<f32x4 *>(orow + d0 + at) =
-            f32x4{W.o[rt][at][c], W.o[rt][at + 1][c], W.o[rt][at + 2][c], W.o[rt][at + 3][c]};
+    for (int rt = 0; rt < NT; ++rt) {
+      const float lsum = sum_across_groups(W.l_run[rt]);
+      if (q4 == 0) {
+        sm.m[wave][rt * 16 + i16] = W.m_run[rt];
+        sm.l[wave][rt * 16 + i16] = lsum;
+      }
     }
-  }
-  __syncthreads();
-  merge_o<ROWS, D>(sm, a.part_o + pidx * D, M);
+    __syncthreads();
+    const size_t pidx = (size_t)part * M;
+    merge_stats<ROWS, D>(sm, a.part_ml + pidx * 2, M);
+    // O^T tile `at`, register c holds row (rt*16 + i16), d = DPL*(4*q4 + c) + at.
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      float *orow = &sm.o[wave][rt * 16 + i16][0];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int d0 = DPL * (4 * q4 + c);
+#pragma unroll
+        for (int at = 0; at < DPL; at += 4)
+          *reinterpret_cast<f32x4 *>(orow + d0 + at) =
+              f32x4{W.o[rt][at][c], W.o[rt][at + 1][c], W.o[rt][at + 2][c], W.o[rt][at + 3][c]};
+      }
+    }
+    __syncthreads();
+    merge_o<ROWS, D>(sm, a.part_o + pidx * D, M);
+  });
 }
 
 }  // namespace vg

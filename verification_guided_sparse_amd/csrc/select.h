@@ -71,38 +71,6 @@ struct SelArgs {
   SelWs ws;
 };
 
-// Inclusive prefix sum across the 64 lanes of a wave with DPP: shifts by
-// 1, 2, 4, 8 inside each 16-lane row (lanes without a source read 0), then the
-// last lane of row 0 (resp. of row 1) is broadcast into rows 1 and 3 (resp.
-// rows 2 and 3).
-__device__ __forceinline__ int wave_inclusive_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
-  return x;
-}
-
-// Exclusive prefix sum over a 256-thread block; `total` receives the sum.
-__device__ __forceinline__ int block_exclusive_scan(int v, int *sm4, int &total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int x = wave_inclusive_scan(v);
-  if (lane == 63) sm4[w] = x;
-  __syncthreads();
-  int pre = 0;
-  total = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = sm4[i];
-    pre += (i < w) ? c : 0;
-    total += c;
-  }
-  __syncthreads();
-  return pre + x - v;
-}
-
 // Given a histogram in LDS (nbins, higher bin = larger key) and a rank k >= 1,
 // find the bin holding the k-th largest key.  Returns the bin and, in `above`,
 // the number of keys in higher bins.  Block-wide; every thread gets the result.

@@ -3,6 +3,7 @@
 // include/vegas_attn.h for the contract of every entry point.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -18,16 +19,7 @@ namespace {
 using namespace vg;
 
 constexpr size_t kAlign = 256;
-#ifndef VG_TARGET_WGS
-#define VG_TARGET_WGS 256
-#endif
-constexpr int kTargetWorkgroups = VG_TARGET_WGS;  // verify: one resident workgroup (4 waves, 2 tiles in flight each) per CU
-// Partial bytes per (b, g) up to which the last split workgroup combines in the
-// same launch (one workgroup reads them all, so only small ones); larger ones
-// get a combine launch with one workgroup per output row.
-#ifndef VG_SPARSE_SPLIT
-#define VG_SPARSE_SPLIT 128  // minimum sparse split length (MFMA path)
-#endif
+constexpr int kCUs = 256;  // MI355X compute units
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -62,10 +54,24 @@ bool use_mfma(const vg_shape *s) {
   return s->dtype == VG_DTYPE_BF16 && s->kernel != VG_KERNEL_VALU;
 }
 
-// Launch plan and workspace layout of one attention call.
+#ifndef VG_VERIFY_PF
+#define VG_VERIFY_PF 2   // tiles in flight per wave, D = 128
+#endif
+#ifndef VG_VERIFY_PF64
+#define VG_VERIFY_PF64 4  // D = 64: half-size tiles, twice as many in flight
+#endif
+#ifndef VG_SPARSE_PF
+#define VG_SPARSE_PF 1
+#endif
+
+// Launch plan and workspace layout of one attention call.  Verify lists are
+// long and may be ragged: the workgroups share their tiles evenly (stream-K).
+// Sparse draft lists are short and the call is latency-bound: fixed splits,
+// which need no length lookup before the first load, unless there are too
+// many splits for one wave of workgroups.
 struct AttnPlan {
-  int rows, nt, mr, splits, split_tokens;
-  bool mfma, ok;  // ok: the key list fits kMaxSplits splits
+  int rows, nt, mr, tile, workgroups, split_tokens, splits;
+  bool mfma, ok;  // ok: batch and tile counts within the kernels' limits
   size_t off_part_o, off_part_ml, bytes;
 };
 
@@ -76,32 +82,35 @@ AttnPlan plan_attention(const vg_shape *s, int nrows, long long max_len, bool sp
   p.nt = (p.rows + 15) / 16;
   p.mr = p.rows <= 16 ? 16 : (p.rows <= 32 ? 32 : 64);
   p.mfma = use_mfma(s);
-  const int unit = p.mfma ? kWaves * 32 : kWaves * kWave;  // entries per workgroup pass
+  p.tile = p.mfma ? 32 : kWave;
   const long long bg = (long long)s->batch * s->num_kv_heads;
-  const long long len = max_len > 0 ? max_len : 1;
-  if (sparse) {
-    const long long mult = (len * bg) / ((long long)unit * 2048);
-    p.split_tokens = unit * (int)(mult > 1 ? mult : 1);
-    if (p.mfma && p.split_tokens < VG_SPARSE_SPLIT) p.split_tokens = VG_SPARSE_SPLIT;
+  const long long L = max_len > 0 ? max_len : 1;
+  long long n_part;
+  // Sparse draft lists are short: fixed splits of one tile per wave while they
+  // fit one wave of resident workgroups, else shared tiles like verify.
+  const long long unit = (long long)kWaves * p.tile;
+  p.ok = s->batch <= kMaxBatch && bg * ((L + p.tile - 1) / p.tile) < (1LL << 31);
+  const long long fixed_wgs = bg * ((L + unit - 1) / unit);
+  // the MFMA kernel with one tile in flight and at most 2 row tiles fits 2
+  // workgroups per CU, the other variants 1
+  const bool two_per_cu = p.mfma && sparse && VG_SPARSE_PF == 1 && p.nt <= 2;
+  const long long resident = (long long)kCUs * (two_per_cu ? 2 : 1);
+  if (sparse && fixed_wgs <= resident) {
+    p.split_tokens = (int)unit;
+    p.splits = (int)((L + unit - 1) / unit);
+    p.workgroups = (int)fixed_wgs;
+    n_part = p.workgroups;
   } else {
-    const long long per = (kTargetWorkgroups + bg - 1) / bg;
-    long long st = (len + per - 1) / per;
-    st = (st + unit - 1) / unit * unit;
-    p.split_tokens = (int)(st > unit ? st : unit);
+    // one wave of resident workgroups, at least one tile per wave
+    const long long tiles = bg * ((L + p.tile - 1) / p.tile);
+    p.workgroups = (int)std::min<long long>((tiles + kWaves - 1) / kWaves, resident);
+    p.split_tokens = 0;
+    p.splits = 0;
+    n_part = p.workgroups + bg;
   }
-  // at most kMaxSplits splits per (b, g): the combine keeps their (m, l) in LDS
-  const long long min_st = ((len + kMaxSplits - 1) / kMaxSplits + unit - 1) / unit * unit;
-  if (p.split_tokens < min_st) p.split_tokens = (int)min_st;
-  // a split's slots (sparse) or page ids (verify) are staged in kSlotSm LDS
-  // entries; splits stay whole multiples of the workgroup pass
-  const long long max_st = (sparse ? kSlotSm : (long long)(kSlotSm - 1) * kPageSize) / unit * unit;
-  if (p.split_tokens > max_st) p.split_tokens = (int)max_st;
-  p.splits = ceil_div(len, p.split_tokens);
-  p.ok = p.splits <= kMaxSplits;
-  const size_t n_part = (size_t)bg * p.splits * p.rows;
   p.off_part_o = 0;
-  p.off_part_ml = align_up(n_part * s->head_dim * sizeof(float));
-  p.bytes = p.off_part_ml + align_up(n_part * 2 * sizeof(float));
+  p.off_part_ml = align_up((size_t)n_part * p.rows * s->head_dim * sizeof(float));
+  p.bytes = p.off_part_ml + align_up((size_t)n_part * p.rows * 2 * sizeof(float));
   return p;
 }
 
@@ -109,19 +118,14 @@ float effective_scale(const vg_shape *s) {
   return s->softmax_scale > 0.f ? s->softmax_scale : 1.0f / std::sqrt((float)s->head_dim);
 }
 
-#ifndef VG_VERIFY_PF
-#define VG_VERIFY_PF 2
-#endif
-#ifndef VG_SPARSE_PF
-#define VG_SPARSE_PF 1
-#endif
 
 template <int D, int NT>
 void launch_mfma_nt(const AttnArgs &a, dim3 grid, hipStream_t st) {
   if (a.sparse)
     hipLaunchKernelGGL((attn_mfma_kernel<D, NT, VG_SPARSE_PF>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<D, NT, VG_VERIFY_PF>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NT, D == 128 ? VG_VERIFY_PF : VG_VERIFY_PF64>), grid,
+                       dim3(kThreads), 0, st, a);
 }
 
 template <int D>
@@ -143,15 +147,19 @@ void launch_valu_t(int mr, const AttnArgs &a, dim3 grid, hipStream_t st) {
   }
 }
 
-// Split kernel, then one combine block per (row, KV head, sequence).
+// Attention kernel over the shared key lists, then one combine block per
+// (row, KV head, sequence).
 vg_status launch_attention(const vg_shape *s, const AttnPlan &p, AttnArgs &a, char *ws,
                            hipStream_t st) {
   a.part_o = reinterpret_cast<float *>(ws + p.off_part_o);
   a.part_ml = reinterpret_cast<float *>(ws + p.off_part_ml);
-  a.splits = p.splits;
+  a.batch = s->batch;
+  a.workgroups = p.workgroups;
+  a.tile = p.tile;
   a.split_tokens = p.split_tokens;
+  a.splits = p.splits;
   a.rows = p.rows;
-  const dim3 grid(p.splits, s->num_kv_heads, s->batch);
+  const dim3 grid(p.workgroups);
   if (p.mfma) {
     if (s->head_dim == 128) launch_mfma_d<128>(p.nt, a, grid, st);
     else launch_mfma_d<64>(p.nt, a, grid, st);

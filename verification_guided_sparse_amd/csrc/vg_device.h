@@ -70,6 +70,38 @@ __device__ __forceinline__ float sum_within_group(float v) {
   v += dpp<kDppRowMirror>(v);
   return v;
 }
+// Inclusive prefix sum across the 64 lanes of a wave with DPP: shifts by
+// 1, 2, 4, 8 inside each 16-lane row (lanes without a source read 0), then the
+// last lane of row 0 (resp. of row 1) is broadcast into rows 1 and 3 (resp.
+// rows 2 and 3).
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+// Exclusive prefix sum over a 256-thread block (4 waves); `total` receives the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *sm4, int &total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int x = wave_inclusive_scan(v);
+  if (lane == 63) sm4[w] = x;
+  __syncthreads();
+  int pre = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = sm4[i];
+    pre += (i < w) ? c : 0;
+    total += c;
+  }
+  __syncthreads();
+  return pre + x - v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -101,12 +133,15 @@ struct AttnArgs {
   float *out;               // [B][nrows][Hq][D]
   float *logits;            // [B][2][Hq][max_prefix] or null
   float *group;             // [B][Hkv][max_prefix] or null
-  float *part_o;            // [B][Hkv][splits][M][D]
-  float *part_ml;           // [B][Hkv][splits][M][2]
+  float *part_o;            // [parts][M][D], parts = workgroups + B * Hkv
+  float *part_ml;           // [parts][M][2]
   int32_t max_pages, max_k, max_prefix;
-  int32_t nrows, gamma;
+  int32_t batch, nrows, gamma;
   int32_t num_q_heads, num_kv_heads, group_size, rows;  // rows = M = nrows * G
-  int32_t splits, split_tokens;
+  int32_t workgroups;       // attention workgroups (grid size)
+  int32_t tile;             // entries per tile of the attention kernel
+  int32_t split_tokens;     // > 0: fixed splits of this many entries (see attn_common.h)
+  int32_t splits;           // splits per (sequence, KV head) when split_tokens > 0
   float scale;       // logit = scale * q.k (natural-log units)
   float scale_log2;  // scale * log2(e)
   int32_t sparse;
@@ -140,9 +175,38 @@ __device__ __forceinline__ int32_t entry_slot(const AttnArgs &a, int b, const Se
   return a.page_table[(size_t)b * a.max_pages + (pos >> 4)] * kPageSize + (pos & (kPageSize - 1));
 }
 
-__device__ __forceinline__ int num_splits_for(const AttnArgs &a, int len) {
-  int n = (len + a.split_tokens - 1) / a.split_tokens;
-  return n < a.splits ? n : a.splits;
+// Work decomposition shared by the attention and combine kernels, for the key
+// lists of the (sequence b, KV head g) segments, seg = b * Hkv + g:
+//  * shared tiles (split_tokens == 0): the lists are cut in tiles and
+//    concatenated; workgroup w of W takes tiles [w * T / W, (w + 1) * T / W) of
+//    the T in total, whatever the sequence lengths (stream-K).  A workgroup's
+//    share of one segment yields one partial result at index w + seg: along the
+//    staircase of (w, seg) pairs each step raises w, seg or both, so these
+//    indices are distinct and below W + B * Hkv.  Finding the shares needs the
+//    lengths of all lists (one dependent load before any other).
+//  * fixed splits (split_tokens > 0): workgroup w = seg * splits + sp takes
+//    entries [sp * split_tokens, (sp + 1) * split_tokens) of its segment's list
+//    and writes partial w, an empty one if the list is shorter.  Nothing
+//    depends on the lengths, which suits short, latency-bound lists.
+constexpr int kMaxBatch = 1024;
+
+// pre[b] = sum over b' < b of ceil(len_b' / tile), for b <= B (LDS, all threads).
+__device__ __forceinline__ void load_tile_prefix(const AttnArgs &a, int *pre, int *sm4) {
+  int run = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += 256) {
+    const int b = b0 + (int)threadIdx.x;
+    const int n = b < a.batch ? (seq_list(a, b).len + a.tile - 1) / a.tile : 0;
+    int tot;
+    const int ex = block_exclusive_scan(n, sm4, tot);
+    if (b < a.batch) pre[b] = run + ex;
+    run += tot;
+  }
+  if (threadIdx.x == 0) pre[a.batch] = run;
+  __syncthreads();
+}
+
+__host__ __device__ inline long long share_begin(int w, long long T, int W) {
+  return (long long)w * T / W;
 }
 
 }  // namespace vg

@@ -23,25 +23,31 @@ class DeviceCase:
     """One workload resident on the GPU, with every buffer the path writes."""
 
     def __init__(self, case: Case, device="cuda", kernel=vg.VG_KERNEL_AUTO, max_tail=None,
-                 like: "DeviceCase | None" = None):
+                 like: "DeviceCase | None" = None, pad=64):
         """`like`: another DeviceCase of the same workload whose inputs are copied on
-        the device (a separate copy of the KV cache, e.g. another layer)."""
+        the device (a separate copy of the KV cache, e.g. another layer).
+        `pad`: export / score rows are padded to a multiple of `pad` floats."""
         self.case = case
         self.device = torch.device(device)
         dev = self.device
         c = case
         self.B, self.Hq, self.Hkv, self.D = c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim
         self.gamma, self.R = c.gamma, c.rows
-        self.max_prefix, self.max_k = c.max_prefix, max(c.max_k, 1)
+        self.max_prefix, self.max_k = -(-max(c.max_prefix, 1) // pad) * pad, max(c.max_k, 1)
         self.dtype = vg.VG_DTYPE_BF16 if c.dtype == "bf16" else vg.VG_DTYPE_F32
+        # room in the page-table rows for the padded max_prefix (entries past a
+        # sequence's pages are -1 and never used)
+        self.max_pages = max(c.max_pages, -(-(self.max_prefix + self.R) // c.page_size))
         self.shape = vg.make_shape(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
-                                   c.max_pages, self.dtype, c.scale, kernel, c.page_size)
+                                   self.max_pages, self.dtype, c.scale, kernel, c.page_size)
         if like is None:
             self.q = _dev(c.q, dev)
             self.q_draft = _dev(c.q_draft, dev)  # [gamma][B][Hq][D]
             self.k_cache = _dev(c.k_cache, dev)
             self.v_cache = _dev(c.v_cache, dev)
-            self.page_table = _dev(c.page_table, dev)
+            pt = np.full((c.batch, self.max_pages), -1, dtype=np.int32)
+            pt[:, : c.max_pages] = c.page_table
+            self.page_table = _dev(pt, dev)
             self.prefix_len = _dev(c.prefix_len, dev)
             self.k = _dev(c.k, dev)
         else:
@@ -49,7 +55,7 @@ class DeviceCase:
                 setattr(self, n, getattr(like, n).clone())
         f32 = dict(dtype=torch.float32, device=dev)
         i32 = dict(dtype=torch.int32, device=dev)
-        mp = max(self.max_prefix, 1)
+        mp = self.max_prefix
         self.out = torch.zeros(self.B, self.R, self.Hq, self.D, **f32)
         self.logits = torch.zeros(self.B, 2, self.Hq, mp, **f32)
         self.group = torch.zeros(self.B, self.Hkv, mp, **f32)
@@ -94,7 +100,7 @@ class DeviceCase:
         flags = vg.VG_TOPK_PREPASS_DONE if prepass_done else 0
         vg.vg_topk_select(self.B, self.scores if scores is None else scores, self.max_prefix,
                           self.prefix_len, self.k, self.max_k, self.page_table, self.case.page_size,
-                          self.case.max_pages, self.sel_pos, self.sel_slot, self.sel_count, flags,
+                          self.max_pages, self.sel_pos, self.sel_slot, self.sel_count, flags,
                           self.ws_select, self.ws_select_bytes, stream)
 
     def sparse(self, step=0, q=None, sel_slot=None, sel_count=None, tail_start=None, tail_len=None,
@@ -119,5 +125,21 @@ class DeviceCase:
             self.sparse(step=s, stream=stream)
 
     # ------------------------------------------------------------- host copies
+    _PADDED = ("logits", "group", "scores")  # last dim padded past the case's max_prefix
+
     def host(self, name):
-        return getattr(self, name).detach().cpu().numpy()
+        """Host copy of a device buffer (padded rows trimmed to the case's max_prefix)."""
+        a = getattr(self, name).detach().cpu().numpy()
+        if name in self._PADDED:
+            a = a[..., : self.case.max_prefix]
+        return a
+
+    def put(self, name, array):
+        """Copy a host array into the leading part of a device buffer."""
+        import torch
+        t = torch.from_numpy(np.ascontiguousarray(array))
+        dst = getattr(self, name)
+        if name in self._PADDED:
+            dst[..., : t.shape[-1]].copy_(t)
+        else:
+            dst.copy_(t)
