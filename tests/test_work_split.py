@@ -109,7 +109,8 @@ def test_stream_k_random(harness):
         assert pieces == model_stream_k(lens, Hkv, tile, W), (lens, Hkv, tile, W)
 
 
-@pytest.mark.parametrize("lens,Hkv,split", [([5250], 8, 128), ([838, 6548, 10], 2, 128), ([7, 1], 4, 256)])
+@pytest.mark.parametrize("lens,Hkv,split", [([5250], 8, 128), ([838, 6548, 10], 2, 128), ([7, 1], 4, 256),
+                                             ([5250], 8, 165), ([3283] * 4, 8, 411), ([9, 40], 2, 13)])
 def test_fixed_pieces(harness, lens, Hkv, split):
     splits = -(-max(lens) // split)
     W = len(lens) * Hkv * splits

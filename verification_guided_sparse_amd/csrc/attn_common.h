@@ -25,11 +25,19 @@ struct MergeSmem {
 };
 
 // Step 1: each wave has written m[w][row] (log2 domain) and l[w][row] (full row
-// sums).  Computes the per-wave weights f = exp2(m_w - max_w m_w) and writes
-// this piece's (m, l) for rows < M to part_ml.  Call between barriers.
+// sums).  Computes the per-wave weights f = exp2(m_w - max_w m_w) into LDS and
+// returns this piece's (m, l) for row t = threadIdx.x (meaningful for t < M).
+// Call between barriers.  The caller stores the pair with store_stats after
+// merge_o: a global store here would make the O writes that follow wait for it
+// (the registers it reads are reused), a full memory round trip.
+struct RowStat {
+  float m, l;
+};
+
 template <int ROWS, int D>
-__device__ __forceinline__ void merge_stats(MergeSmem<ROWS, D> &sm, float *part_ml, int M) {
+__device__ __forceinline__ RowStat merge_stats(MergeSmem<ROWS, D> &sm) {
   const int t = threadIdx.x;
+  RowStat r{kMInit, 0.f};
   if (t < ROWS) {
     float mx = sm.m[0][t];
 #pragma unroll
@@ -41,11 +49,15 @@ __device__ __forceinline__ void merge_stats(MergeSmem<ROWS, D> &sm, float *part_
       sm.f[w][t] = f;
       l += f * sm.l[w][t];
     }
-    if (t < M) {
-      part_ml[2 * t + 0] = mx;
-      part_ml[2 * t + 1] = l;
-    }
+    r.m = mx;
+    r.l = l;
   }
+  return r;
+}
+
+__device__ __forceinline__ void store_stats(float *part_ml, int M, RowStat r) {
+  const int t = threadIdx.x;
+  if (t < M) *reinterpret_cast<float2 *>(part_ml + 2 * t) = float2{r.m, r.l};
 }
 
 // Step 2: each wave has written its O (unscaled) to sm.o[w].  Writes the

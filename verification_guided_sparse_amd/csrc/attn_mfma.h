@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kThreads, (PF == 1 && NT <= 2) ? 2 : 1) void attn_m
     }
     __syncthreads();
     const size_t pidx = (size_t)part * M;
-    merge_stats<ROWS, D>(sm, a.part_ml + pidx * 2, M);
+    const RowStat st = merge_stats<ROWS, D>(sm);
     // O^T tile `at`, register c holds row (rt*16 + i16), d = DPL*(4*q4 + c) + at.
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
@@ -440,6 +440,7 @@ __global__ __launch_bounds__(kThreads, (PF == 1 && NT <= 2) ? 2 : 1) void attn_m
     }
     __syncthreads();
     merge_o<ROWS, D>(sm, a.part_o + pidx * D, M);
+    store_stats(a.part_ml + pidx * 2, M, st);
   });
 }
 

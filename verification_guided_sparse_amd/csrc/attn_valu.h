@@ -181,13 +181,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_valu_kernel(AttnArgs a) {
     }
     __syncthreads();
     const size_t pidx = (size_t)part * M;
-    merge_stats<MR, D>(sm.merge, a.part_ml + pidx * 2, M);
+    const RowStat st = merge_stats<MR, D>(sm.merge);
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
       for (int k = 0; k < DV; ++k) sm.merge.o[wave][m][lane * DV + k] = o[m][k];
     __syncthreads();
     merge_o<MR, D>(sm.merge, a.part_o + pidx * D, M);
+    store_stats(a.part_ml + pidx * 2, M, st);
   });
 }
 

@@ -61,14 +61,12 @@ bool use_mfma(const vg_shape *s) {
 #define VG_VERIFY_PF64 4  // D = 64: half-size tiles, twice as many in flight
 #endif
 #ifndef VG_SPARSE_PF
-#define VG_SPARSE_PF 1
+#define VG_SPARSE_PF 1   // tiles in flight per wave, sparse draft
 #endif
 
 // Launch plan and workspace layout of one attention call.  Verify lists are
 // long and may be ragged: the workgroups share their tiles evenly (stream-K).
-// Sparse draft lists are short and the call is latency-bound: fixed splits,
-// which need no length lookup before the first load, unless there are too
-// many splits for one wave of workgroups.
+// Sparse draft lists are short: fixed splits.
 struct AttnPlan {
   int rows, nt, mr, tile, workgroups, split_tokens, splits;
   bool mfma, ok;  // ok: batch and tile counts within the kernels' limits
@@ -86,24 +84,23 @@ AttnPlan plan_attention(const vg_shape *s, int nrows, long long max_len, bool sp
   const long long bg = (long long)s->batch * s->num_kv_heads;
   const long long L = max_len > 0 ? max_len : 1;
   long long n_part;
-  // Sparse draft lists are short: fixed splits of one tile per wave while they
-  // fit one wave of resident workgroups, else shared tiles like verify.
-  const long long unit = (long long)kWaves * p.tile;
   p.ok = s->batch <= kMaxBatch && bg * ((L + p.tile - 1) / p.tile) < (1LL << 31);
-  const long long fixed_wgs = bg * ((L + unit - 1) / unit);
-  // the MFMA kernel with one tile in flight and at most 2 row tiles fits 2
-  // workgroups per CU, the other variants 1
-  const bool two_per_cu = p.mfma && sparse && VG_SPARSE_PF == 1 && p.nt <= 2;
-  const long long resident = (long long)kCUs * (two_per_cu ? 2 : 1);
-  if (sparse && fixed_wgs <= resident) {
-    p.split_tokens = (int)unit;
-    p.splits = (int)((L + unit - 1) / unit);
-    p.workgroups = (int)fixed_wgs;
+  if (sparse) {
+    // Sparse draft lists are short and the call is latency-bound: fixed splits
+    // of 4 tiles (one per wave) while the workgroups fit one wave of residency
+    // (2 per CU), else of 8 tiles.  Fixed splits need no length lookup before
+    // the first load; workgroups past a list's end exit after writing an empty
+    // partial, and the hardware dispatcher balances ragged batches.
+    const long long unit = (long long)kWaves * p.tile;
+    const bool small = bg * ((L + unit - 1) / unit) <= 2LL * kCUs;
+    p.split_tokens = (int)(small ? unit : 2 * unit);
+    p.splits = (int)((L + p.split_tokens - 1) / p.split_tokens);
+    p.workgroups = (int)(bg * p.splits);
     n_part = p.workgroups;
   } else {
-    // one wave of resident workgroups, at least one tile per wave
+    // one wave of resident workgroups (1 per CU), at least one tile per wave
     const long long tiles = bg * ((L + p.tile - 1) / p.tile);
-    p.workgroups = (int)std::min<long long>((tiles + kWaves - 1) / kWaves, resident);
+    p.workgroups = (int)std::min<long long>((tiles + kWaves - 1) / kWaves, kCUs);
     p.split_tokens = 0;
     p.splits = 0;
     n_part = p.workgroups + bg;
