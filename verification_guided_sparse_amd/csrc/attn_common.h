@@ -57,7 +57,7 @@ __device__ __forceinline__ RowStat merge_stats(MergeSmem<ROWS, D> &sm) {
 
 __device__ __forceinline__ void store_stats(float *part_ml, int M, RowStat r) {
   const int t = threadIdx.x;
-  if (t < M) *reinterpret_cast<float2 *>(part_ml + 2 * t) = float2{r.m, r.l};
+  if (t < M) *reinterpret_cast<f32x2 *>(part_ml + 2 * t) = f32x2{r.m, r.l};
 }
 
 // Step 2: each wave has written its O (unscaled) to sm.o[w].  Writes the

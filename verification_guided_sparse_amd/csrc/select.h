@@ -3,21 +3,28 @@
 // Scores map to order-preserving 32-bit keys (larger score <-> larger key;
 // -0.0 is folded onto +0.0).  The k-th largest key K* is found by a radix
 // select over key bits [20,32) / [10,20) / [0,10), every pass spread over
-// chunks of 2048 positions (one workgroup each):
+// chunks of 2048 positions:
 //
-//   pass 1  LDS histogram of bits [20,32) per chunk, merged into the
-//           sequence's global histogram with atomics (optionally fused with
-//           the aggregation that produces the scores).  Also clears the
-//           bits [10,20) histogram pass 2 fills.
-//   pass 2  each chunk finds the bin b1 holding K*, counts its entries above
-//           b1, stages its candidates (bin == b1) in position order and adds
-//           their bits [10,20) to a second global histogram.
-//   pass 3  each chunk finds b2 from the second histogram, resolves the last
-//           10 bits on the (few) candidates, derives from the candidate list
-//           how many entries every earlier chunk selects -- hence its own
-//           output offset -- and writes its selected positions ascending
+//   pass 1  (one workgroup per chunk) LDS histogram of bits [20,32), merged
+//           into the sequence's global histogram with atomics (optionally
+//           fused with the aggregation that produces the scores).  Also clears
+//           the bits [10,20) histogram pass 2 fills.  (More workgroups per
+//           chunk make the atomics on the busiest bins contend.)
+//   pass 2  (one workgroup per chunk) finds the bin b1 holding K*, counts the
+//           chunk's entries above b1, stages its candidates (bin == b1) in
+//           position order and adds their bits [10,20) to a second global
+//           histogram.
+//   pass 3  (one workgroup per chunk) finds b2 from the second histogram,
+//           resolves the last 10 bits on the candidates (a fixed group of
+//           threads per chunk reads that chunk's candidates), counts per chunk
+//           the candidates above and equal to K*, derives its own output offset
+//           from those counts, and writes its selected positions ascending
 //           (keys > K*, then keys == K* lowest position first) with their
 //           page-size-1 slots.  Chunk 0 clears the first histogram.
+//
+// Ties at K* are taken in position order, so the ties taken before a point
+// are min(ties, equal keys before it): one scan of (greater, equal) counts
+// gives every output offset.
 //
 // Workgroups hand data to one another only across kernel boundaries; both
 // histograms are zero between calls.
@@ -28,7 +35,7 @@
 namespace vg {
 
 constexpr int kSelThreads = 256;
-constexpr int kChunk = 2048;                   // positions per pass workgroup
+constexpr int kChunk = 2048;                   // positions per pass-2/3 workgroup
 constexpr int kPerThread = kChunk / kSelThreads;  // 8 consecutive positions per thread
 constexpr int kBins1 = 4096;                   // key bits [20, 32)
 constexpr int kBins23 = 1024;                  // key bits [10, 20), then [0, 10)
@@ -71,41 +78,54 @@ struct SelArgs {
   SelWs ws;
 };
 
-// Given a histogram in LDS (nbins, higher bin = larger key) and a rank k >= 1,
-// find the bin holding the k-th largest key.  Returns the bin and, in `above`,
-// the number of keys in higher bins.  Block-wide; every thread gets the result.
-__device__ __forceinline__ int find_bin(const uint32_t *h, int nbins, int k, int *sm4, int *sm_res,
-                                        int &above) {
-  const int per = nbins / kSelThreads;  // bins per thread (4 or 16)
+// Rank search over a histogram held in registers: thread t holds the PER bins
+// [nbins - PER (t + 1), nbins - PER t) in descending order (h[0] = the
+// highest).  Finds the bin holding the k-th largest key (1 <= k <= total) and,
+// in `above`, the number of keys in higher bins.  Block-wide; every thread gets
+// the result.  `res` (2 ints of LDS) must not be shared with a call whose
+// results are still being read.
+template <int PER>
+__device__ __forceinline__ int find_bin_regs(const uint32_t (&h)[PER], int nbins, int k, int *sm4,
+                                             int *res, int &above) {
   const int t = threadIdx.x;
-  // thread t owns bins [nbins - per*(t+1), nbins - per*t), scanned from the top
-  const int top = nbins - per * t;
+  const int top = nbins - PER * t;
   int local = 0;
-  for (int i = 1; i <= per; ++i) local += (int)h[top - i];
-  int total;
-  const int pre = block_exclusive_scan(local, sm4, total);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) local += (int)h[i];
   if (t == 0) {
-    sm_res[0] = 0;
-    sm_res[1] = 0;
+    res[0] = 0;
+    res[1] = 0;
   }
-  __syncthreads();
+  int total;
+  const int pre = block_exclusive_scan(local, sm4, total);  // its barriers order the reset above
   if (pre < k && k <= pre + local) {
     int run = pre;
-    for (int i = 1; i <= per; ++i) {
-      const int c = (int)h[top - i];
-      if (k <= run + c) {
-        sm_res[0] = top - i;
-        sm_res[1] = run;
-        break;
+    bool done = false;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = (int)h[i];
+      if (!done && k <= run + c) {
+        res[0] = top - 1 - i;
+        res[1] = run;
+        done = true;
       }
       run += c;
     }
   }
   __syncthreads();
-  above = sm_res[1];
-  const int bin = sm_res[0];
-  __syncthreads();
-  return bin;
+  above = res[1];
+  return res[0];
+}
+
+// Thread t's PER descending bins of a global (or LDS) histogram of nbins.
+template <int PER>
+__device__ __forceinline__ void load_bins_desc(const uint32_t *hist, int nbins, uint32_t (&h)[PER]) {
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(hist + nbins - PER * (threadIdx.x + 1));
+  u32x4 v[PER / 4];
+#pragma unroll
+  for (int i = 0; i < PER / 4; ++i) v[i] = src[i];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) h[i] = v[(PER - 1 - i) / 4][(PER - 1 - i) % 4];
 }
 
 // Pass 1.  grid (nchunks, B).  AGG: compute scores from src and write them.
@@ -189,24 +209,9 @@ __global__ __launch_bounds__(kSelThreads) void select_pass1_kernel(SelArgs a) {
     if (lh[i]) atomicAdd(&gh[i], lh[i]);
 }
 
-// Load a sequence's bits [20,32) histogram into LDS (16 bins per thread, four
-// 16-byte loads in flight together) and find the bin of the k-th largest key.
-__device__ __forceinline__ uint32_t load_hist_find_b1(const uint32_t *gh, uint32_t *lh, int k_eff,
-                                                      int *sm4, int *sm_res, int &above1) {
-  const int t = threadIdx.x;
-  const u32x4 *g4 = reinterpret_cast<const u32x4 *>(gh) + 4 * t;
-  u32x4 h4[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) h4[i] = g4[i];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4 *>(lh)[4 * t + i] = h4[i];
-  __syncthreads();
-  return (uint32_t)find_bin(lh, kBins1, k_eff, sm4, sm_res, above1);
-}
-
 // Pass 2.  grid (nchunks, B).
 __global__ __launch_bounds__(kSelThreads) void select_pass2_kernel(SelArgs a) {
-  __shared__ uint32_t lh[kBins1];
+  __shared__ uint32_t lh[kBins23];
   __shared__ int sm4[4];
   __shared__ int sm_res[2];
   const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
@@ -216,18 +221,23 @@ __global__ __launch_bounds__(kSelThreads) void select_pass2_kernel(SelArgs a) {
   if (w >= nch) return;
   const int j0 = w * kChunk + t * kPerThread;
   const float *srow = a.scores + (size_t)b * a.max_prefix;
-  float sv[kPerThread];  // issued before the histogram work so the loads overlap it
+  float sv[kPerThread];  // issued first: independent of everything below
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) sv[i] = (j0 + i < P) ? srow[j0 + i] : 0.f;
+  reinterpret_cast<u32x4 *>(lh)[t] = u32x4{0u, 0u, 0u, 0u};  // candidates' bits [10,20)
   uint32_t b1 = 0xffffffffu;  // k_eff == 0: nothing above, no candidates
   int above1 = 0;
-  if (k_eff > 0) b1 = load_hist_find_b1(a.ws.hist1 + (size_t)b * kBins1, lh, k_eff, sm4, sm_res, above1);
+  if (k_eff > 0) {
+    uint32_t h[16];
+    load_bins_desc<16>(a.ws.hist1 + (size_t)b * kBins1, kBins1, h);
+    b1 = (uint32_t)find_bin_regs<16>(h, kBins1, k_eff, sm4, sm_res, above1);  // also orders the clear
+  } else {
+    __syncthreads();
+  }
   if (w == 0 && t == 0) {
     a.ws.state[4 * b + 0] = (int)b1;
     a.ws.state[4 * b + 1] = above1;
   }
-  for (int i = t; i < kBins23; i += kSelThreads) lh[i] = 0u;  // candidates' bits [10,20)
-  __syncthreads();
   uint32_t key[kPerThread];
   int n_above = 0, n_cand = 0;
 #pragma unroll
@@ -239,9 +249,11 @@ __global__ __launch_bounds__(kSelThreads) void select_pass2_kernel(SelArgs a) {
     n_cand += cand;
     if (cand) atomicAdd(&lh[(key[i] >> 10) & 1023u], 1u);
   }
-  int tot_above, tot_cand;
-  block_exclusive_scan(n_above, sm4, tot_above);
-  int off = block_exclusive_scan(n_cand, sm4, tot_cand);
+  // one scan of both counts (each <= 2048)
+  int tot;
+  int off = block_exclusive_scan(n_above | (n_cand << 16), sm4, tot);
+  const int tot_above = tot & 0xffff, tot_cand = tot >> 16;
+  off >>= 16;
   u32x2 *cst = a.ws.cand + (size_t)b * a.max_prefix + (size_t)w * kChunk;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i)
@@ -250,20 +262,23 @@ __global__ __launch_bounds__(kSelThreads) void select_pass2_kernel(SelArgs a) {
     a.ws.above[(size_t)b * kMaxChunks + w] = tot_above;
     a.ws.ncand[(size_t)b * kMaxChunks + w] = tot_cand;
   }
+  // the scan's barriers ordered the LDS histogram atomics before these reads
   uint32_t *h2 = a.ws.hist2 + (size_t)b * kBins23;
-  for (int i = t; i < kBins23; i += kSelThreads)
-    if (lh[i]) atomicAdd(&h2[i], lh[i]);
+  const u32x4 v = reinterpret_cast<const u32x4 *>(lh)[t];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (v[c]) atomicAdd(&h2[4 * t + c], v[c]);
 }
 
 // Pass 3.  grid (nchunks, B).
 __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
   __shared__ uint32_t lh[kBins23];
-  __shared__ int csum[kMaxChunks + 1];   // candidate offsets per chunk
-  __shared__ int nsel[kMaxChunks];       // entries each chunk selects
-  __shared__ int neq[kMaxChunks];        // candidates equal to K* per chunk
+  __shared__ int csum[kMaxChunks + 1];  // candidate offsets per chunk
+  __shared__ int cgt[kMaxChunks];       // per chunk: candidates above K*
+  __shared__ int ceq[kMaxChunks];       // per chunk: candidates equal to K*
   __shared__ u32x2 cache[kCandCache];
   __shared__ int sm4[4];
-  __shared__ int sm_res[2];
+  __shared__ int sm_res[8];
   const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
   const int P = a.prefix_len[b];
   const int k_eff = min(a.k[b], P);
@@ -273,11 +288,16 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
     return;
   }
   if (w >= nch) return;
+  // ---- loads that depend on nothing else, issued first
   const int j0 = w * kChunk + t * kPerThread;
   const float *srow = a.scores + (size_t)b * a.max_prefix;
-  float sv[kPerThread];  // issued first: independent of everything below
+  float sv[kPerThread];
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) sv[i] = (j0 + i < P) ? srow[j0 + i] : 0.f;
+  // the page of this thread's 8 positions (one page when page_size is a multiple of 8)
+  const bool one_page = (a.page_size & 7) == 0;
+  int page = 0;
+  if (a.sel_slot && one_page && j0 < P) page = a.page_table[(size_t)b * a.max_pages + j0 / a.page_size];
   if (w == 0) {  // every reader of hist1 has finished (pass 2): clear it for the next call
     u32x4 *g4 = reinterpret_cast<u32x4 *>(a.ws.hist1 + (size_t)b * kBins1) + 4 * t;
 #pragma unroll
@@ -287,8 +307,9 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
   if (k_eff <= 0) return;
   const uint32_t b1 = (uint32_t)a.ws.state[4 * b + 0];
   const int above1 = a.ws.state[4 * b + 1];
-  // hist2 (4 bins per thread) and the per-chunk counts, loaded together
-  const u32x4 h4 = reinterpret_cast<const u32x4 *>(a.ws.hist2 + (size_t)b * kBins23)[t];
+  uint32_t h2[4];
+  load_bins_desc<4>(a.ws.hist2 + (size_t)b * kBins23, kBins23, h2);
+  // per-chunk counts: thread t owns chunks t * per + i
   const int per = (nch + kSelThreads - 1) / kSelThreads;  // <= 4
   int ab[4], nc[4];
 #pragma unroll
@@ -298,7 +319,7 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
     ab[i] = ok ? a.ws.above[(size_t)b * kMaxChunks + c] : 0;
     nc[i] = ok ? a.ws.ncand[(size_t)b * kMaxChunks + c] : 0;
   }
-  reinterpret_cast<u32x4 *>(lh)[t] = h4;
+  reinterpret_cast<u32x4 *>(lh)[t] = u32x4{0u, 0u, 0u, 0u};  // bits [0,10) of the candidates
   {
     int local = 0;
 #pragma unroll
@@ -311,143 +332,147 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
       if (i < per && c < nch) {
         csum[c] = run;
         run += nc[i];
-        nsel[c] = 0;
-        neq[c] = 0;
       }
     }
     if (t == 0) csum[nch] = tot;
   }
-  __syncthreads();
   const int k1 = k_eff - above1;  // >= 1: rank of K* inside bin b1
   int above2;
-  const uint32_t b2 = (uint32_t)find_bin(lh, kBins23, k1, sm4, sm_res, above2);
+  const uint32_t b2 = (uint32_t)find_bin_regs<4>(h2, kBins23, k1, sm4, sm_res, above2);  // csum visible after
   const int k2 = k1 - above2;
   const uint32_t pre22 = (b1 << 10) | b2;
   const int n_c = csum[nch];
   const u32x2 *cand = a.ws.cand + (size_t)b * a.max_prefix;
-  auto cand_global = [&](int gi) -> u32x2 {  // candidate number gi, chunk order
-    int lo = 0, hi = nch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (csum[mid] <= gi) lo = mid; else hi = mid - 1;
-    }
-    return cand[(size_t)lo * kChunk + (gi - csum[lo])];
-  };
   const bool cached = n_c <= kCandCache;
+  // Candidates of chunk c are read by a fixed group of tpc consecutive threads
+  // (tpc = 256 / nch rounded down to a power of two, at most a wave; for
+  // nch > 256 every thread takes chunks t, t + 256, ...): no search for a
+  // candidate's chunk.
+  int tpc = 1;
+  while (tpc < kWave && tpc * 2 * nch <= kSelThreads) tpc *= 2;
+  const int sub = t % tpc, c_first = t / tpc, c_step = kSelThreads / tpc;
   if (cached) {
-    constexpr int U = 8;
-    for (int base = 0; base < n_c; base += kSelThreads * U) {
-      u32x2 v[U];
+    for (int c = c_first; c < nch; c += c_step) {
+      const int n = csum[c + 1] - csum[c];
+      for (int i0 = sub; i0 < n; i0 += tpc * 8) {
+        u32x2 v[8];
 #pragma unroll
-      for (int i = 0; i < U; ++i) {
-        const int gi = base + i * kSelThreads + t;
-        v[i] = gi < n_c ? cand_global(gi) : u32x2{0u, 0u};
-      }
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * tpc;
+          v[u] = i < n ? cand[(size_t)c * kChunk + i] : u32x2{0u, 0u};
+        }
 #pragma unroll
-      for (int i = 0; i < U; ++i) {
-        const int gi = base + i * kSelThreads + t;
-        if (gi < n_c) cache[gi] = v[i];
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * tpc;
+          if (i < n) cache[csum[c] + i] = v[u];
+        }
       }
     }
+    __syncthreads();
   }
-  for (int i = t; i < kBins23; i += kSelThreads) lh[i] = 0u;
-  __syncthreads();
-  auto candidate = [&](int gi) -> u32x2 { return cached ? cache[gi] : cand_global(gi); };
+  auto candidate = [&](int c, int i) -> u32x2 {
+    return cached ? cache[csum[c] + i] : cand[(size_t)c * kChunk + i];
+  };
   // bits [0, 10) among candidates sharing the 22-bit prefix of K*
-  for (int gi = t; gi < n_c; gi += kSelThreads) {
-    const u32x2 e = candidate(gi);
-    if ((e[0] >> 10) == pre22) atomicAdd(&lh[e[0] & 1023u], 1u);
+  for (int c = c_first; c < nch; c += c_step) {
+    const int n = csum[c + 1] - csum[c];
+    for (int i = sub; i < n; i += tpc) {
+      const u32x2 e = candidate(c, i);
+      if ((e[0] >> 10) == pre22) atomicAdd(&lh[e[0] & 1023u], 1u);
+    }
   }
   __syncthreads();
+  uint32_t h3[4];
+  load_bins_desc<4>(lh, kBins23, h3);
   int above3;
-  const uint32_t b3 = (uint32_t)find_bin(lh, kBins23, k2, sm4, sm_res, above3);
+  const uint32_t b3 = (uint32_t)find_bin_regs<4>(h3, kBins23, k2, sm4, sm_res + 2, above3);
   const uint32_t kstar = (pre22 << 10) | b3;
   const int ties = k2 - above3;  // entries equal to K* to keep, lowest positions first
-  // per chunk: candidates above K* and candidates equal to K*
-  for (int gi = t; gi < n_c; gi += kSelThreads) {
-    const u32x2 e = candidate(gi);
-    const int c = (int)(e[1] / kChunk);
-    if (e[0] > kstar) atomicAdd(&nsel[c], 1);
-    else if (e[0] == kstar) atomicAdd(&neq[c], 1);
+  // per chunk: candidates above and equal to K*, summed over the chunk's group
+  for (int c = c_first; c < nch; c += c_step) {
+    const int n = csum[c + 1] - csum[c];
+    int gt = 0, eq = 0;
+    for (int i = sub; i < n; i += tpc) {
+      const u32x2 e = candidate(c, i);
+      gt += e[0] > kstar;
+      eq += e[0] == kstar;
+    }
+    // the group is tpc consecutive lanes of one wave (tpc <= 64 divides 64)
+    for (int o = 1; o < tpc; o <<= 1) {
+      gt += __shfl_xor(gt, o);
+      eq += __shfl_xor(eq, o);
+    }
+    if (sub == 0) {
+      cgt[c] = gt;
+      ceq[c] = eq;
+    }
   }
   __syncthreads();
-  // Per chunk c: taken_c = ties left after the chunks before it, capped by its
-  // own equal candidates; selected_c = above_c + (candidates > K*) + taken_c.
-  // The thread owning chunk w publishes the exclusive prefixes at w.
-  int eq_before, sel_before;
+  // Output offset of chunk w: entries above K* in earlier chunks plus the ties
+  // they take, min(ties, equal keys in earlier chunks).
+  int sel_before, eq_before;
   {
-    int eqv[4], eq_local = 0;
+    int gv[4], ev[4], g_local = 0, e_local = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = t * per + i;
-      eqv[i] = (i < per && c < nch) ? neq[c] : 0;
-      eq_local += eqv[i];
+      const bool ok = i < per && c < nch;
+      gv[i] = ok ? ab[i] + cgt[c] : 0;
+      ev[i] = ok ? ceq[c] : 0;
+      g_local += gv[i];
+      e_local += ev[i];
     }
-    int tot;
-    int eq_run = block_exclusive_scan(eq_local, sm4, tot);
-    int selv[4], sel_local = 0, eq_at[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = t * per + i;
-      eq_at[i] = eq_run;
-      selv[i] = 0;
-      if (i < per && c < nch) {
-        const int taken = max(0, min(eqv[i], ties - eq_run));
-        selv[i] = ab[i] + nsel[c] + taken;
-      }
-      sel_local += selv[i];
-      eq_run += eqv[i];
-    }
-    int sel_run = block_exclusive_scan(sel_local, sm4, tot);
+    int gt_tot, eq_tot;
+    int g_run = block_exclusive_scan(g_local, sm4, gt_tot);
+    int e_run = block_exclusive_scan(e_local, sm4, eq_tot);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = t * per + i;
       if (i < per && c == w) {
-        sm_res[0] = sel_run;
-        sm_res[1] = eq_at[i];
+        sm_res[4] = g_run + min(ties, e_run);
+        sm_res[5] = e_run;
       }
-      sel_run += selv[i];
+      g_run += gv[i];
+      e_run += ev[i];
     }
     __syncthreads();
-    sel_before = sm_res[0];
-    eq_before = sm_res[1];
-    __syncthreads();
+    sel_before = sm_res[4];
+    eq_before = sm_res[5];
   }
-  // Select this chunk's entries in position order.
+  // Select this chunk's entries in position order: one scan of the packed
+  // (greater, equal) counts (each <= 2048) gives every thread's offset.
   uint32_t key[kPerThread];
-  int n_eq = 0;
+  int n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     key[i] = (j0 + i < P) ? score_key(sv[i]) : 0u;
+    n_gt += (j0 + i < P) && (key[i] > kstar);
     n_eq += (j0 + i < P) && (key[i] == kstar);
   }
-  int tot_eq;
-  int tie_rank = eq_before + block_exclusive_scan(n_eq, sm4, tot_eq);
-  bool sel[kPerThread];
-  int n_sel = 0;
+  int tot;
+  const int ex = block_exclusive_scan(n_gt | (n_eq << 16), sm4, tot);
+  const int gt_before = ex & 0xffff, eq_in = ex >> 16;
+  const int tie_budget = max(0, ties - eq_before);  // ties left for this chunk
+  int eq_rank = eq_in;
+  int oi = sel_before + gt_before + min(tie_budget, eq_in);
+  const int cap = min(k_eff, a.max_k);
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     bool s = false;
     if (j0 + i < P) {
       if (key[i] > kstar) s = true;
-      else if (key[i] == kstar) s = (tie_rank++ < ties);
+      else if (key[i] == kstar) s = (eq_rank++ < tie_budget);
     }
-    sel[i] = s;
-    n_sel += s;
-  }
-  int tot_sel;
-  int oi = sel_before + block_exclusive_scan(n_sel, sm4, tot_sel);
-  const int cap = min(k_eff, a.max_k);
-#pragma unroll
-  for (int i = 0; i < kPerThread; ++i)
-    if (sel[i] && oi < cap) {
+    if (s && oi < cap) {
       const int pos = j0 + i;
       a.sel_pos[(size_t)b * a.max_k + oi] = pos;
-      if (a.sel_slot)
-        a.sel_slot[(size_t)b * a.max_k + oi] =
-            a.page_table[(size_t)b * a.max_pages + pos / a.page_size] * a.page_size + pos % a.page_size;
-      ++oi;
+      if (a.sel_slot) {
+        const int pg = one_page ? page : a.page_table[(size_t)b * a.max_pages + pos / a.page_size];
+        a.sel_slot[(size_t)b * a.max_k + oi] = pg * a.page_size + pos % a.page_size;
+      }
     }
+    oi += s;
+  }
 }
 
 }  // namespace vg
