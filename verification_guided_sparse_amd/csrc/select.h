@@ -128,84 +128,97 @@ __device__ __forceinline__ void load_bins_desc(const uint32_t *hist, int nbins, 
   for (int i = 0; i < PER; ++i) h[i] = v[(PER - 1 - i) / 4][(PER - 1 - i) % 4];
 }
 
-// Pass 1.  grid (nchunks, B).  AGG: compute scores from src and write them.
-// HIST: add the chunk's bits [20,32) histogram to the global one.
+// Pass 1.  grid (nchunks, B), kP1Threads threads (kP1Per consecutive positions
+// each).  AGG: compute scores from src and write them.  HIST: add the chunk's
+// bits [20,32) histogram to the global one.
+#ifndef VG_P1_THREADS
+#define VG_P1_THREADS 1024
+#endif
+constexpr int kP1Threads = VG_P1_THREADS;
+constexpr int kP1Per = kChunk / kP1Threads;  // 8, 4 or 2
+typedef float p1vec __attribute__((ext_vector_type(kP1Per < 4 ? kP1Per : 4)));
+constexpr int kP1Vec = kP1Per < 4 ? kP1Per : 4;  // floats per load
+constexpr int kP1Loads = kP1Per / kP1Vec;       // loads per row
+
 template <bool AGG, bool HIST>
-__global__ __launch_bounds__(kSelThreads) void select_pass1_kernel(SelArgs a) {
+__global__ __launch_bounds__(kP1Threads) void select_pass1_kernel(SelArgs a) {
   __shared__ uint32_t lh[kBins1];
   const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
   const int P = a.prefix_len[b];
   const int nch = (P + kChunk - 1) / kChunk;
   if (w >= nch) return;
   if (HIST) {
-    for (int i = t; i < kBins1; i += kSelThreads) lh[i] = 0u;
-    __syncthreads();
+    for (int i = t; i < kBins1 / 4; i += kP1Threads) reinterpret_cast<u32x4 *>(lh)[i] = u32x4{0u, 0u, 0u, 0u};
   }
-  const int j0 = w * kChunk + t * kPerThread;
-  float sc[kPerThread];
-  if (AGG) {
+  const int j0 = w * kChunk + t * kP1Per;
+  float sc[kP1Per];
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) sc[i] = 0.f;
-    const bool vec = ((a.max_prefix & 3) == 0) && (j0 + kPerThread <= P);
+  for (int i = 0; i < kP1Per; ++i) sc[i] = 0.f;
+  if (AGG) {
+    const bool vec = ((a.max_prefix % kP1Vec) == 0) && (j0 + kP1Per <= P);
     // rows (t, h) of src in order; batches of 8 rows whose loads are in flight together
     const int nrow = a.src_rows * a.src_heads;
     const float *base = a.src + (size_t)b * nrow * a.max_prefix;
     if (vec) {
       constexpr int U = 8;
       for (int r0 = 0; r0 < nrow; r0 += U) {
-        f32x4 v[U][2];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (r0 + u < nrow) {
-            const float *row = base + (size_t)(r0 + u) * a.max_prefix + j0;
-            v[u][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row));
-            v[u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 4));
-          } else {
-            v[u][0] = v[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-        }
+        p1vec v[U][kP1Loads];
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sc[i] += v[u][0][i];
-            sc[4 + i] += v[u][1][i];
-          }
+          for (int q = 0; q < kP1Loads; ++q)
+            v[u][q] = (r0 + u < nrow) ? __builtin_nontemporal_load(reinterpret_cast<const p1vec *>(
+                                            base + (size_t)(r0 + u) * a.max_prefix + j0 + q * kP1Vec))
+                                      : p1vec{};
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int q = 0; q < kP1Loads; ++q)
+#pragma unroll
+            for (int i = 0; i < kP1Vec; ++i) sc[q * kP1Vec + i] += v[u][q][i];
       }
     } else {
       for (int r = 0; r < nrow; ++r) {
         const float *row = base + (size_t)r * a.max_prefix;
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i)
+        for (int i = 0; i < kP1Per; ++i)
           if (j0 + i < P) sc[i] += row[j0 + i];
       }
     }
     float *dst = a.scores_out + (size_t)b * a.max_prefix;
     if (vec) {
-      *reinterpret_cast<f32x4 *>(dst + j0) = f32x4{sc[0], sc[1], sc[2], sc[3]};
-      *reinterpret_cast<f32x4 *>(dst + j0 + 4) = f32x4{sc[4], sc[5], sc[6], sc[7]};
+#pragma unroll
+      for (int q = 0; q < kP1Loads; ++q) {
+        p1vec o;
+#pragma unroll
+        for (int i = 0; i < kP1Vec; ++i) o[i] = sc[q * kP1Vec + i];
+        *reinterpret_cast<p1vec *>(dst + j0 + q * kP1Vec) = o;
+      }
     } else {
 #pragma unroll
-      for (int i = 0; i < kPerThread; ++i)
+      for (int i = 0; i < kP1Per; ++i)
         if (j0 + i < P) dst[j0 + i] = sc[i];
     }
   } else {
     const float *srow = a.scores + (size_t)b * a.max_prefix;
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) sc[i] = (j0 + i < P) ? srow[j0 + i] : 0.f;
+    for (int i = 0; i < kP1Per; ++i) sc[i] = (j0 + i < P) ? srow[j0 + i] : 0.f;
   }
   if (!HIST) return;
 
   if (w == 0) {  // pass 2 of this call fills hist2: start it from zero
     uint32_t *h2 = a.ws.hist2 + (size_t)b * kBins23;
-    for (int i = t; i < kBins23; i += kSelThreads) h2[i] = 0u;
+    for (int i = t; i < kBins23; i += kP1Threads) h2[i] = 0u;
   }
+  __syncthreads();  // the LDS histogram is clear
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i)
+  for (int i = 0; i < kP1Per; ++i)
     if (j0 + i < P) atomicAdd(&lh[score_key(sc[i]) >> 20], 1u);
   __syncthreads();
+  // consecutive lanes take consecutive bins: one atomic instruction then
+  // touches as few cache lines as possible
   uint32_t *gh = a.ws.hist1 + (size_t)b * kBins1;
-  for (int i = t; i < kBins1; i += kSelThreads)
+  for (int i = t; i < kBins1; i += kP1Threads)
     if (lh[i]) atomicAdd(&gh[i], lh[i]);
 }
 
@@ -262,12 +275,11 @@ __global__ __launch_bounds__(kSelThreads) void select_pass2_kernel(SelArgs a) {
     a.ws.above[(size_t)b * kMaxChunks + w] = tot_above;
     a.ws.ncand[(size_t)b * kMaxChunks + w] = tot_cand;
   }
-  // the scan's barriers ordered the LDS histogram atomics before these reads
+  // the scan's barriers ordered the LDS histogram atomics before these reads;
+  // consecutive lanes take consecutive bins
   uint32_t *h2 = a.ws.hist2 + (size_t)b * kBins23;
-  const u32x4 v = reinterpret_cast<const u32x4 *>(lh)[t];
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-    if (v[c]) atomicAdd(&h2[4 * t + c], v[c]);
+  for (int i = t; i < kBins23; i += kSelThreads)
+    if (lh[i]) atomicAdd(&h2[i], lh[i]);
 }
 
 // Pass 3.  grid (nchunks, B).
@@ -294,10 +306,22 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
   float sv[kPerThread];
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) sv[i] = (j0 + i < P) ? srow[j0 + i] : 0.f;
-  // the page of this thread's 8 positions (one page when page_size is a multiple of 8)
-  const bool one_page = (a.page_size & 7) == 0;
-  int page = 0;
-  if (a.sel_slot && one_page && j0 < P) page = a.page_table[(size_t)b * a.max_pages + j0 / a.page_size];
+  // page ids of this thread's 8 positions, loaded now: a load among the output
+  // stores at the end would make each store wait for the ones before it
+  // (loads and stores retire in order on one counter)
+  int page[kPerThread] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const bool one_page = (a.page_size & 7) == 0;  // then the 8 positions share a page
+  if (a.sel_slot) {
+    const int32_t *prow = a.page_table + (size_t)b * a.max_pages;
+    if (one_page) {
+      const int pg = j0 < P ? prow[j0 / a.page_size] : 0;
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) page[i] = pg;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) page[i] = j0 + i < P ? prow[(j0 + i) / a.page_size] : 0;
+    }
+  }
   if (w == 0) {  // every reader of hist1 has finished (pass 2): clear it for the next call
     u32x4 *g4 = reinterpret_cast<u32x4 *>(a.ws.hist1 + (size_t)b * kBins1) + 4 * t;
 #pragma unroll
@@ -373,12 +397,17 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
   auto candidate = [&](int c, int i) -> u32x2 {
     return cached ? cache[csum[c] + i] : cand[(size_t)c * kChunk + i];
   };
-  // bits [0, 10) among candidates sharing the 22-bit prefix of K*
+  // bits [0, 10) among candidates sharing the 22-bit prefix of K* (reads in
+  // batches of 4, all in flight together)
   for (int c = c_first; c < nch; c += c_step) {
     const int n = csum[c + 1] - csum[c];
-    for (int i = sub; i < n; i += tpc) {
-      const u32x2 e = candidate(c, i);
-      if ((e[0] >> 10) == pre22) atomicAdd(&lh[e[0] & 1023u], 1u);
+    for (int i0 = sub; i0 < n; i0 += 4 * tpc) {
+      uint32_t kq[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kq[u] = i0 + u * tpc < n ? candidate(c, i0 + u * tpc)[0] : 0u;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + u * tpc < n && (kq[u] >> 10) == pre22) atomicAdd(&lh[kq[u] & 1023u], 1u);
     }
   }
   __syncthreads();
@@ -392,10 +421,15 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
   for (int c = c_first; c < nch; c += c_step) {
     const int n = csum[c + 1] - csum[c];
     int gt = 0, eq = 0;
-    for (int i = sub; i < n; i += tpc) {
-      const u32x2 e = candidate(c, i);
-      gt += e[0] > kstar;
-      eq += e[0] == kstar;
+    for (int i0 = sub; i0 < n; i0 += 4 * tpc) {
+      uint32_t kq[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kq[u] = i0 + u * tpc < n ? candidate(c, i0 + u * tpc)[0] : 0u;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        gt += (i0 + u * tpc < n) && kq[u] > kstar;
+        eq += (i0 + u * tpc < n) && kq[u] == kstar;
+      }
     }
     // the group is tpc consecutive lanes of one wave (tpc <= 64 divides 64)
     for (int o = 1; o < tpc; o <<= 1) {
@@ -454,8 +488,14 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
   const int gt_before = ex & 0xffff, eq_in = ex >> 16;
   const int tie_budget = max(0, ties - eq_before);  // ties left for this chunk
   int eq_rank = eq_in;
-  int oi = sel_before + gt_before + min(tie_budget, eq_in);
-  const int cap = min(k_eff, a.max_k);
+  // rank of this thread's first selected entry inside the chunk
+  int li = gt_before + min(tie_budget, eq_in);
+  const int n_sel = (tot & 0xffff) + min(tie_budget, tot >> 16);  // the chunk's selections
+  // Stage the chunk's selected positions (and their page ids) in LDS in order
+  // -- at most 2048; the candidate cache is free again -- then write them out
+  // with consecutive lanes on consecutive outputs.
+  int *st_pos = reinterpret_cast<int *>(cache);  // its readers finished before the scans above
+  int *st_page = st_pos + kChunk;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     bool s = false;
@@ -463,15 +503,20 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
       if (key[i] > kstar) s = true;
       else if (key[i] == kstar) s = (eq_rank++ < tie_budget);
     }
-    if (s && oi < cap) {
-      const int pos = j0 + i;
-      a.sel_pos[(size_t)b * a.max_k + oi] = pos;
-      if (a.sel_slot) {
-        const int pg = one_page ? page : a.page_table[(size_t)b * a.max_pages + pos / a.page_size];
-        a.sel_slot[(size_t)b * a.max_k + oi] = pg * a.page_size + pos % a.page_size;
-      }
+    if (s) {
+      st_pos[li] = j0 + i;
+      st_page[li] = page[i];
     }
-    oi += s;
+    li += s;
+  }
+  __syncthreads();
+  const int n_out = min(n_sel, min(k_eff, a.max_k) - sel_before);
+  int32_t *pos_row = a.sel_pos + (size_t)b * a.max_k + sel_before;
+  int32_t *slot_row = a.sel_slot ? a.sel_slot + (size_t)b * a.max_k + sel_before : nullptr;
+  for (int q = t; q < n_out; q += kSelThreads) {
+    const int pos = st_pos[q];
+    pos_row[q] = pos;
+    if (slot_row) slot_row[q] = st_page[q] * a.page_size + pos % a.page_size;
   }
 }
 

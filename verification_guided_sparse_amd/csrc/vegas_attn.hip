@@ -315,9 +315,9 @@ vg_status vg_aggregate_scores(int32_t batch, const float *src, int32_t src_rows,
     const SelPlan p = plan_select(batch, max_prefix);
     if (!aligned16(select_ws) || select_ws_bytes < p.bytes) return VG_ERR_WORKSPACE;
     a.ws = sel_ws(p, select_ws);
-    hipLaunchKernelGGL((select_pass1_kernel<true, true>), grid, dim3(kSelThreads), 0, st, a);
+    hipLaunchKernelGGL((select_pass1_kernel<true, true>), grid, dim3(kP1Threads), 0, st, a);
   } else {
-    hipLaunchKernelGGL((select_pass1_kernel<true, false>), grid, dim3(kSelThreads), 0, st, a);
+    hipLaunchKernelGGL((select_pass1_kernel<true, false>), grid, dim3(kP1Threads), 0, st, a);
   }
   return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
 }
@@ -363,7 +363,7 @@ vg_status vg_topk_select(int32_t batch, const float *scores, int32_t max_prefix,
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid(ceil_div(max_prefix > 0 ? max_prefix : 1, kChunk), batch);
   if (!(flags & VG_TOPK_PREPASS_DONE))
-    hipLaunchKernelGGL((select_pass1_kernel<false, true>), grid, dim3(kSelThreads), 0, st, a);
+    hipLaunchKernelGGL((select_pass1_kernel<false, true>), grid, dim3(kP1Threads), 0, st, a);
   hipLaunchKernelGGL(select_pass2_kernel, grid, dim3(kSelThreads), 0, st, a);
   hipLaunchKernelGGL(select_pass3_kernel, grid, dim3(kSelThreads), 0, st, a);
   return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
