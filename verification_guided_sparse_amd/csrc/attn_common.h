@@ -266,18 +266,18 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 
 // Calls fn(b, g, part, e_begin, e_end) for each piece of this workgroup's work
 // (uniform across the block).  With fixed splits a workgroup past its list's
-// end gets one empty piece (e_begin == e_end).  pre / sm4: LDS for
+// end gets one empty piece (e_begin == e_end).  pre / lens / sm4: LDS for
 // load_tile_prefix.
 template <typename Fn>
-__device__ __forceinline__ void for_each_piece(const AttnArgs &a, int *pre, int *sm4, Fn fn) {
+__device__ __forceinline__ void for_each_piece(const AttnArgs &a, int *pre, int *lens, int *sm4, Fn fn) {
   const int W = a.workgroups, w = blockIdx.x, Hkv = a.num_kv_heads;
   const bool fixed = a.split_tokens > 0;
   ShareWalk s{0, 1, 0};
   if (!fixed) {
-    load_tile_prefix(a, pre, sm4);
+    load_tile_prefix(a, pre, sm4, lens);  // lists' lengths kept in LDS: no second load
     s = share_walk_begin(pre, a.batch, Hkv, w, W);
   }
-  auto len = [&](int b) { return seq_list(a, b).len; };
+  auto len = [&](int b) { return fixed ? seq_list(a, b).len : lens[b]; };
   // One call site for fn, so that it is inlined once.
   while (s.t < s.t_end) {
     Piece p;

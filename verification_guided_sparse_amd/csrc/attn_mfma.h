@@ -326,8 +326,13 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
 
 // PF = tiles in flight per wave.  PF == 1: load, then compute, two waves per
 // SIMD; PF > 1: a ring of PF tiles, one wave per SIMD.
-template <int D, int NT, int PF>
-__global__ __launch_bounds__(kThreads, (PF == 1 && NT <= 2) ? 2 : 1) void attn_mfma_kernel(AttnArgs a) {
+// SPARSE selects the sparse draft (true) or verify (false) instantiation; the
+// local copy of the arguments carries it as a constant, so every helper that
+// tests a.sparse folds to one path.
+template <int D, int NT, int PF, bool SPARSE>
+__global__ __launch_bounds__(kThreads, (PF == 1 && NT <= 2) ? 2 : 1) void attn_mfma_kernel(AttnArgs a_in) {
+  AttnArgs a = a_in;
+  a.sparse = SPARSE ? 1 : 0;
   constexpr int KS = D / 32;   // k-steps of the QK^T contraction
   constexpr int DPL = D / 16;  // d values per lane per V row, = number of PV tiles
   constexpr int ROWS = NT * 16;
@@ -338,6 +343,7 @@ __global__ __launch_bounds__(kThreads, (PF == 1 && NT <= 2) ? 2 : 1) void attn_m
   MergeSmem<ROWS, D> &sm = lds.m;
   __shared__ int slot_sm[kSlotSm];
   __shared__ int pre[kMaxBatch + 1];
+  __shared__ int lens[kMaxBatch];
   __shared__ int sm4[4];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -346,10 +352,22 @@ __global__ __launch_bounds__(kThreads, (PF == 1 && NT <= 2) ? 2 : 1) void attn_m
   const bool do_export = !a.sparse && (a.logits != nullptr || a.group != nullptr);
   const bool vec_export = (a.max_prefix & 3) == 0;
   const int chunk = a.sparse ? kSparseChunk : kVerifyChunk;
+  // Fixed sparse splits (at most kThreads entries, one chunk): this
+  // workgroup's part of the explicit slot list is loaded now, together with
+  // the list length rather than after it.  Entries past the selection count
+  // are loaded (they are inside the [B][max_k] list) but never used.
+  const bool pref = a.sparse && a.split_tokens > 0 && a.split_tokens <= kThreads;
+  int pf_slot = 0;
+  if (pref) {
+    const int seg = blockIdx.x / a.splits;
+    const int e = (blockIdx.x % a.splits) * a.split_tokens + (int)threadIdx.x;
+    if ((int)threadIdx.x < a.split_tokens && e < a.max_k)
+      pf_slot = a.sel_slot[(size_t)(seg / a.num_kv_heads) * a.max_k + e];
+  }
 
-  for_each_piece(a, pre, sm4, [&](int b, int g, int part, int e_begin, int e_end) {
-    const SeqList s = seq_list(a, b);
-    WaveState<D, NT> W;
+  // Query fragments of (sequence b, KV head g): lane (q4, i16) holds row
+  // rt * 16 + i16, d-chunks 4 * ks + q4.
+  auto load_q = [&](int b, int g, u32x4 (&qf)[NT][KS]) {
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
       const int row = rt * 16 + i16;
@@ -358,12 +376,34 @@ __global__ __launch_bounds__(kThreads, (PF == 1 && NT <= 2) ? 2 : 1) void attn_m
         const uint16_t *qrow =
             static_cast<const uint16_t *>(a.q) + ((size_t)(b * a.nrows + r) * Hq + h) * D;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          W.qf[rt][ks] = *reinterpret_cast<const u32x4 *>(qrow + (4 * ks + q4) * 8);
+        for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = *reinterpret_cast<const u32x4 *>(qrow + (4 * ks + q4) * 8);
       } else {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) W.qf[rt][ks] = u32x4{0u, 0u, 0u, 0u};
+        for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = u32x4{0u, 0u, 0u, 0u};
       }
+    }
+  };
+  // With fixed sparse splits the queries too are loaded before the list length.
+  u32x4 q_pre[NT][KS];
+  if (pref) {
+    const int seg = blockIdx.x / a.splits;
+    load_q(seg / a.num_kv_heads, seg % a.num_kv_heads, q_pre);
+  }
+
+  for_each_piece(a, pre, lens, sm4, [&](int b, int g, int part, int e_begin, int e_end) {
+    const SeqList s = seq_list(a, b);
+    WaveState<D, NT> W;
+    if (pref) {
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) W.qf[rt][ks] = q_pre[rt][ks];
+    } else {
+      load_q(b, g, W.qf);
+    }
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      const int row = rt * 16 + i16;
       W.m_run[rt] = kMInit;
       W.l_run[rt] = 0.f;
       const int r = row / G;
@@ -378,7 +418,11 @@ __global__ __launch_bounds__(kThreads, (PF == 1 && NT <= 2) ? 2 : 1) void attn_m
     for (int c0 = e_begin; c0 < e_end; c0 += chunk) {
       const int c1 = min(e_end, c0 + chunk);
       __syncthreads();  // earlier users of slot_sm / the K staging area are done
-      stage_slots(slot_sm, a, b, s, c0, c1);
+      if (pref) {  // the one chunk starts at e_begin = this split's first entry
+        if ((int)threadIdx.x < min(c1, s.cnt) - c0) slot_sm[threadIdx.x] = pf_slot;
+      } else {
+        stage_slots(slot_sm, a, b, s, c0, c1);
+      }
       __syncthreads();
       // This wave's tiles: j = 0 .. nw-1 cover entries c0 + 32 * (wave + 4 j).
       const int ntiles = (c1 - c0 + 31) / 32;
@@ -426,9 +470,11 @@ __global__ __launch_bounds__(kThreads, (PF == 1 && NT <= 2) ? 2 : 1) void attn_m
     const size_t pidx = (size_t)part * M;
     const RowStat st = merge_stats<ROWS, D>(sm);
     // O^T tile `at`, register c holds row (rt*16 + i16), d = DPL*(4*q4 + c) + at.
+    // Only the M real rows are written (the draft has 4 of a tile's 16).
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
       float *orow = &sm.o[wave][rt * 16 + i16][0];
+      if (rt * 16 + i16 >= M) continue;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int d0 = DPL * (4 * q4 + c);

@@ -62,6 +62,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_valu_kernel(AttnArgs a) {
   constexpr int CH = Elem<T>::kPer16B;
   __shared__ ValuSmem<MR, D> sm;
   __shared__ int pre[kMaxBatch + 1];
+  __shared__ int lens[kMaxBatch];
   __shared__ int sm4[4];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_valu_kernel(AttnArgs a) {
   const size_t slot_elems = (size_t)Hkv * D;
   const bool do_export = !a.sparse && (a.logits != nullptr || a.group != nullptr);
 
-  for_each_piece(a, pre, sm4, [&](int b, int g, int part, int e_begin, int e_end) {
+  for_each_piece(a, pre, lens, sm4, [&](int b, int g, int part, int e_begin, int e_end) {
     const SeqList s = seq_list(a, b);
     __syncthreads();  // the previous piece's merge has read the LDS
     for (int i = threadIdx.x; i < MR * D; i += kThreads) {

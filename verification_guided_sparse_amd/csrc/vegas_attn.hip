@@ -119,9 +119,9 @@ float effective_scale(const vg_shape *s) {
 template <int D, int NT>
 void launch_mfma_nt(const AttnArgs &a, dim3 grid, hipStream_t st) {
   if (a.sparse)
-    hipLaunchKernelGGL((attn_mfma_kernel<D, NT, VG_SPARSE_PF>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NT, VG_SPARSE_PF, true>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<D, NT, D == 128 ? VG_VERIFY_PF : VG_VERIFY_PF64>), grid,
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NT, D == 128 ? VG_VERIFY_PF : VG_VERIFY_PF64, false>), grid,
                        dim3(kThreads), 0, st, a);
 }
 

@@ -191,12 +191,15 @@ __device__ __forceinline__ int32_t entry_slot(const AttnArgs &a, int b, const Se
 //    depends on the lengths, which suits short, latency-bound lists.
 constexpr int kMaxBatch = 1024;
 
-// pre[b] = sum over b' < b of ceil(len_b' / tile), for b <= B (LDS, all threads).
-__device__ __forceinline__ void load_tile_prefix(const AttnArgs &a, int *pre, int *sm4) {
+// pre[b] = sum over b' < b of ceil(len_b' / tile), for b <= B, and, if `lens`
+// is given, lens[b] = len_b (LDS, all threads).
+__device__ __forceinline__ void load_tile_prefix(const AttnArgs &a, int *pre, int *sm4, int *lens = nullptr) {
   int run = 0;
   for (int b0 = 0; b0 < a.batch; b0 += 256) {
     const int b = b0 + (int)threadIdx.x;
-    const int n = b < a.batch ? (seq_list(a, b).len + a.tile - 1) / a.tile : 0;
+    const int len = b < a.batch ? seq_list(a, b).len : 0;
+    const int n = (len + a.tile - 1) / a.tile;
+    if (lens && b < a.batch) lens[b] = len;
     int tot;
     const int ex = block_exclusive_scan(n, sm4, tot);
     if (b < a.batch) pre[b] = run + ex;
