@@ -58,11 +58,15 @@ bool use_mfma(const vg_shape *s) {
 #define VG_VERIFY_PF 2   // tiles in flight per wave, D = 128
 #endif
 #ifndef VG_VERIFY_PF64
-#define VG_VERIFY_PF64 4  // D = 64: half-size tiles, twice as many in flight
+#define VG_VERIFY_PF64 1  // D = 64: one tile in flight, two workgroups per CU
 #endif
 #ifndef VG_SPARSE_PF
 #define VG_SPARSE_PF 1   // tiles in flight per wave, sparse draft
 #endif
+
+// Tiles in flight per wave of the verify kernel: at D = 128 two (one when 3 or
+// 4 row tiles leave no registers for a second), at D = 64 one.
+constexpr int verify_pf(int D, int NT) { return D == 128 ? (NT <= 2 ? VG_VERIFY_PF : 1) : VG_VERIFY_PF64; }
 
 // Launch plan and workspace layout of one attention call.  Verify lists are
 // long and may be ragged: the workgroups share their tiles evenly (stream-K).
@@ -100,7 +104,9 @@ AttnPlan plan_attention(const vg_shape *s, int nrows, long long max_len, bool sp
   } else {
     // one wave of resident workgroups (1 per CU), at least one tile per wave
     const long long tiles = bg * ((L + p.tile - 1) / p.tile);
-    p.workgroups = (int)std::min<long long>((tiles + kWaves - 1) / kWaves, kCUs);
+    const int occ = !p.mfma ? 1 : attn_occupancy(s->head_dim, p.nt, verify_pf(s->head_dim, p.nt), false);
+    const int resident = occ * kCUs;
+    p.workgroups = (int)std::min<long long>((tiles + kWaves - 1) / kWaves, resident);
     p.split_tokens = 0;
     p.splits = 0;
     n_part = p.workgroups + bg;
@@ -121,8 +127,7 @@ void launch_mfma_nt(const AttnArgs &a, dim3 grid, hipStream_t st) {
   if (a.sparse)
     hipLaunchKernelGGL((attn_mfma_kernel<D, NT, VG_SPARSE_PF, true>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<D, NT, D == 128 ? VG_VERIFY_PF : VG_VERIFY_PF64, false>), grid,
-                       dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<D, NT, verify_pf(D, NT), false>), grid, dim3(kThreads), 0, st, a);
 }
 
 template <int D>
