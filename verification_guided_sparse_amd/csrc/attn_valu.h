@@ -22,25 +22,24 @@ struct Elem;
 template <>
 struct Elem<float> {
   static constexpr int kPer16B = 4;
-  __device__ static void load16(const void *p, float *out) {
-    const f32x4 v = __builtin_nontemporal_load(static_cast<const f32x4 *>(p));
-    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
-  }
   __device__ static float load1(const void *p, size_t i) { return static_cast<const float *>(p)[i]; }
+  __device__ static void convert16(const u32x4 &v, float *out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(v[i]);
+  }
 };
 template <>
 struct Elem<uint16_t> {
   static constexpr int kPer16B = 8;
-  __device__ static void load16(const void *p, float *out) {
-    const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4 *>(p));
+  __device__ static float load1(const void *p, size_t i) {
+    return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
+  }
+  __device__ static void convert16(const u32x4 &v, float *out) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       out[2 * i] = __uint_as_float(v[i] << 16);
       out[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
     }
-  }
-  __device__ static float load1(const void *p, size_t i) {
-    return bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i]);
   }
 };
 
@@ -50,7 +49,6 @@ struct ValuSmem {
     struct {
       float q[MR][D];
       float p[kWaves][MR][kWave];
-      int slot[kWaves][kWave];
     } loop;
     MergeSmem<MR, D> merge;
   };
@@ -95,26 +93,47 @@ __global__ __launch_bounds__(kThreads, 1) void attn_valu_kernel(AttnArgs a) {
     }
 
     const int ntiles = (e_end - e_begin + kWave - 1) / kWave;
+    constexpr int NK = D / CH;  // 16-byte chunks of a K row
+    const T *kbase = static_cast<const T *>(a.k_cache) + (size_t)g * D;
+    const T *vbase = static_cast<const T *>(a.v_cache) + (size_t)g * D + lane * DV;
     for (int t = wave; t < ntiles; t += kWaves) {
       const int e0 = e_begin + t * kWave;
       const int e = e0 + lane;
+      // entries past the end reuse the last one's slot; their p is 0
       const int slot = entry_slot(a, b, s, min(e, e_end - 1));
-      sm.loop.slot[wave][lane] = slot;
+      // This lane's K row, all chunks in flight together.
+      u32x4 kraw[NK];
+      const T *krow = kbase + (size_t)slot * slot_elems;
+#pragma unroll
+      for (int c = 0; c < NK; ++c) kraw[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(krow + c * CH));
 
       float acc[MR];
 #pragma unroll
       for (int m = 0; m < MR; ++m) acc[m] = 0.f;
-      const T *krow = static_cast<const T *>(a.k_cache) + (size_t)slot * slot_elems + (size_t)g * D;
-      for (int d0 = 0; d0 < D; d0 += CH) {
+#pragma unroll
+      for (int c = 0; c < NK; ++c) {
         float kv[CH];
-        Elem<T>::load16(krow + d0, kv);
+        Elem<T>::convert16(kraw[c], kv);
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
-          float sacc = 0.f;
 #pragma unroll
-          for (int c = 0; c < CH; ++c) sacc = fmaf(sm.loop.q[m][d0 + c], kv[c], sacc);
-          acc[m] += sacc;
+          for (int c4 = 0; c4 < CH; c4 += 4) {
+            const f32x4 q4 = *reinterpret_cast<const f32x4 *>(&sm.loop.q[m][c * CH + c4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m] = fmaf(q4[i], kv[c4 + i], acc[m]);
+          }
         }
+      }
+
+      // This lane's DV columns of the 64 V rows (entry j's slot comes from lane
+      // j), issued after QK so that they do not hold registers through it;
+      // they land during the export and softmax.
+      float vv[kWave][DV];
+#pragma unroll
+      for (int j = 0; j < kWave; ++j) {
+        const int sj = __builtin_amdgcn_readlane(slot, j);  // wave-uniform: scalar address
+#pragma unroll
+        for (int k = 0; k < DV; ++k) vv[j][k] = Elem<T>::load1(vbase + (size_t)sj * slot_elems, k);
       }
 
       if (do_export && e0 < s.p_export) {
@@ -134,14 +153,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_valu_kernel(AttnArgs a) {
         if (a.group && e < s.p_export) a.group[(size_t)(b * Hkv + g) * a.max_prefix + e] = gs * a.scale;
       }
 
+      // Softmax with the wave reductions on DPP / lane swaps (no LDS round
+      // trips); the running max and rescale factor are wave-uniform.
       float alpha[MR];
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
         const int vis = s.vis0 + m / G;
         const bool ok = (e < e_end) && (e < vis);
         const float x = ok ? acc[m] * a.scale_log2 : kNegInf;
-        const float m_new = fmaxf(m_run[m], wave_max(x));
-        alpha[m] = exp2_fast(m_run[m] - m_new);
+        const float m_new = __builtin_amdgcn_readfirstlane(fmaxf(m_run[m], wave_max_dpp(x)));
+        alpha[m] = __builtin_amdgcn_readfirstlane(exp2_fast(m_run[m] - m_new));
         m_run[m] = m_new;
         const float p = exp2_fast(x - m_new);
         l_run[m] = l_run[m] * alpha[m] + p;
@@ -154,27 +175,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_valu_kernel(AttnArgs a) {
       for (int m = 0; m < MR; ++m)
 #pragma unroll
         for (int k = 0; k < DV; ++k) o[m][k] *= alpha[m];
-      const int jn = min(kWave, e_end - e0);
-      for (int j = 0; j < jn; ++j) {
-        const int sj = sm.loop.slot[wave][j];
-        const T *vrow = static_cast<const T *>(a.v_cache) + (size_t)sj * slot_elems + (size_t)g * D;
-        float vv[DV];
+      // PV over all 64 entries (masked ones have p = 0 and a real row);
+      // probabilities broadcast from LDS, 4 entries per read
 #pragma unroll
-        for (int k = 0; k < DV; ++k) vv[k] = Elem<T>::load1(vrow, lane * DV + k);
+      for (int j4 = 0; j4 < kWave; j4 += 4) {
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
-          const float p = sm.loop.p[wave][m][j];
+          const f32x4 p4 = *reinterpret_cast<const f32x4 *>(&sm.loop.p[wave][m][j4]);
 #pragma unroll
-          for (int k = 0; k < DV; ++k) o[m][k] = fmaf(p, vv[k], o[m][k]);
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < DV; ++k) o[m][k] = fmaf(p4[i], vv[j4 + i][k], o[m][k]);
         }
       }
       __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
     __syncthreads();  // the merge area aliases the loop buffers
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-      const float lsum = wave_sum(l_run[m]);
+      const float lsum = sum_across_groups(sum_within_group(l_run[m]));
       if (lane == 0) {
         sm.merge.m[wave][m] = m_run[m];
         sm.merge.l[wave][m] = lsum;

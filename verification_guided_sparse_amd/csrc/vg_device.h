@@ -103,6 +103,16 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *sm4, int &total)
   return pre + x - v;
 }
 
+// Max across the 64 lanes without LDS: DPP inside each 16-lane row, then the
+// lane swaps across rows.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppRowMirror>(v));
+  return max_across_groups(v);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
