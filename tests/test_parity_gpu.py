@@ -125,6 +125,8 @@ def _run_chain(c, dc, refs, export):
         p = pos[b, :n].astype(np.int64)
         expect = c.page_table[b, p // c.page_size].astype(np.int64) * c.page_size + p % c.page_size
         _check(parity.exact_gate(slot[b, :n], expect), f"chain[{export}] slot translation seq {b}")
+    if c.gamma == 0:  # no draft steps
+        return
     # last draft step, against the oracle over the GPU's own selection
     s = c.gamma - 1
     o_ref = oracle.sparse(np.ascontiguousarray(c.q_draft[s][:, None]), c.k_cache, c.v_cache,
@@ -146,6 +148,19 @@ SMALL = {
     "c5_small_sharp": lambda: synth.sharp(synth.small("c5_gptoss_64k", prefix=(2000, 2077))),
     "short_prefixes": lambda: synth.small("c2_qwen3_32k", prefix=(1, 5, 17, 33), gamma=4, k_pct=50),
     "short_prefixes_g8": lambda: synth.small("c5_gptoss_64k", prefix=(3, 16, 31, 64), gamma=5, k_pct=50),
+    # gamma = 0: the first draft row and the bonus row are the same row (counted twice)
+    "gamma0": lambda: synth.small("c2_qwen3_32k", prefix=(1500, 1), gamma=0, k_pct=10),
+    # one query head per KV head: plain decode attention
+    "g1_decode": lambda: synth.small("c5_gptoss_64k", prefix=(3000, 700), num_q_heads=8, num_kv_heads=8,
+                                     gamma=2),
+    # 64 ragged sequences under a permuted pool: many work-split segments
+    "many_seqs": lambda: synth.small("c2_qwen3_32k", prefix=tuple(17 + (i * 613) % 1900 for i in range(64)),
+                                     gamma=3, paging="permuted", ramp=0, spans=0),
+    # 64 query rows per KV head at D = 128 (4 row tiles)
+    "rows64_d128": lambda: synth.small("c2_qwen3_32k", prefix=(2100,), num_q_heads=64, num_kv_heads=8,
+                                       gamma=7),
+    # k = P: every prefix position selected
+    "k_all": lambda: synth.small("c5_gptoss_64k", prefix=(300, 77), k_pct=100),
 }
 
 
