@@ -108,6 +108,9 @@ def main():
     ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every step separately")
+    ap.add_argument("--collection", action="store_true",
+                    help="also time the logit export + aggregation for two rows (Collect-2-Query) "
+                         "against every row (full collection)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (HBM byte-counter calibration)")
     args = ap.parse_args()
@@ -229,6 +232,8 @@ def main():
 
     if args.breakdown:
         result["breakdown_us"] = breakdown(layers, c, args.export)
+    if args.collection:
+        result["collection_us"] = collection(layers)
 
     if not args.no_cpu_baseline:
         nthreads = min(16, os.cpu_count() or 1)
@@ -276,6 +281,46 @@ def capture(fn):
         fn()
     torch.cuda.synchronize()
     return g
+
+
+def timed_graph_us(fn, n_layers, reps=5):
+    """Per-layer us of fn (all layers' calls captured in one graph), HIP events."""
+    import torch
+    g = capture(fn)
+    g.replay()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / (reps * n_layers)
+
+
+def collection(layers):
+    """Cost of the logit export + aggregation with Collect-2-Query (rows 0 and gamma)
+    and with full collection (every row), for the raw and the group export: each is
+    verify-with-export minus verify-without-export, plus the aggregation of that
+    export (per layer, us)."""
+    n = len(layers)
+    t = {
+        "verify_none": timed_graph_us(lambda: [lc.verify(export="none") for lc in layers], n),
+        "verify_raw_two": timed_graph_us(lambda: [lc.verify(export="raw") for lc in layers], n),
+        "verify_raw_all": timed_graph_us(lambda: [lc.verify(export="raw", rows="all") for lc in layers], n),
+        "verify_group_two": timed_graph_us(lambda: [lc.verify(export="group") for lc in layers], n),
+        "verify_group_all": timed_graph_us(lambda: [lc.verify(export="group", rows="all") for lc in layers], n),
+        "aggregate_raw_two": timed_graph_us(lambda: [lc.aggregate(src="raw") for lc in layers], n),
+        "aggregate_raw_all": timed_graph_us(lambda: [lc.aggregate(src="raw_all") for lc in layers], n),
+        "aggregate_group": timed_graph_us(lambda: [lc.aggregate(src="group") for lc in layers], n),
+    }
+    out = {k: round(v, 2) for k, v in t.items()}
+    base = t["verify_none"]
+    out["overhead_raw_two"] = round(t["verify_raw_two"] - base + t["aggregate_raw_two"], 2)
+    out["overhead_raw_all"] = round(t["verify_raw_all"] - base + t["aggregate_raw_all"], 2)
+    out["overhead_group_two"] = round(t["verify_group_two"] - base + t["aggregate_group"], 2)
+    out["overhead_group_all"] = round(t["verify_group_all"] - base + t["aggregate_group"], 2)
+    return out
 
 
 def breakdown(layers, c, export):

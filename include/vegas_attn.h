@@ -135,6 +135,26 @@ vg_status vg_verify_attention(const vg_shape *shape, const void *q, const void *
                               float *out, float *logits, float *group_scores, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/*
+ * Verification attention with the full-collection logit export: the logits of
+ * every verify row, i.e. the selection objective of Vegas section 2.A summed
+ * over all gamma+1 verify tokens, which Collect-2-Query (section 2.B) reduces
+ * to two rows.  Provided to measure that reduction.
+ *
+ * Same arguments, preconditions, workspace (vg_verify_workspace_size) and
+ * errors as vg_verify_attention, except the exports:
+ *   logits       [B][gamma+1][Hq][max_prefix] float, nullable: [b][r][h][j] =
+ *                l[r][h][j] for j < P_b; entries j >= P_b are not written.
+ *   group_scores [B][Hkv][max_prefix] float, nullable: sum over all gamma+1
+ *                rows and the G query heads of KV head g, for j < P_b.
+ * vg_aggregate_scores with src_rows = gamma+1 turns the raw form into scores.
+ */
+vg_status vg_verify_attention_all_rows(const vg_shape *shape, const void *q, const void *k_cache,
+                                       const void *v_cache, const int32_t *page_table,
+                                       const int32_t *prefix_len, int32_t max_prefix, int32_t gamma,
+                                       float *out, float *logits, float *group_scores,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------- aggregate */
 
 /*

@@ -90,6 +90,16 @@ def verify(q, k_cache, v_cache, page_table, prefix_len, gamma, scale, *, page_si
     return out, logits, group, lall
 
 
+def group_sums(src, num_kv_heads):
+    """Group form of an export [B][T][Hq][max_prefix]: the sum over its T rows and
+    the G = Hq / Hkv consecutive query heads of each KV head -> [B][Hkv][max_prefix]
+    (the per-KV-head part of the selection objective, Vegas section 2.A)."""
+    src = np.asarray(src, dtype=np.float64)
+    B, T, Hq, mp = src.shape
+    G = Hq // int(num_kv_heads)
+    return src.reshape(B, T, int(num_kv_heads), G, mp).sum(axis=(1, 3))
+
+
 def aggregate(src, prefix_len, max_prefix=None):
     """Scores s[b][j] = sum over rows t and heads h of src[b][t][h][j], j < P_b (else 0).
 

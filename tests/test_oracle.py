@@ -334,3 +334,40 @@ def test_k_rule_reproduces_workload_sizes():
            for n, c in synth.CONFIGS.items() if c.prefix}
     assert got == {"c1_tiny": 205, "c2_qwen3_32k": 1638, "c3_qwen3_128k": 5243, "c5_gptoss_64k": 3277}
     assert math.floor(2048 * 0.02 + 0.5) == synth.pct_round_half_up(2048, 2) == 41
+
+
+def test_full_collection_scores_are_the_literal_objective():
+    """Full collection: every verify row exported; the aggregated score of position j
+    is the per-position coefficient of the section 2.A objective summed over all
+    gamma+1 rows and all heads (independent einsum), and the group form summed over
+    KV heads gives the same scores."""
+    case = _tiny(prefix=(23, 9), gamma=3, hq=8, hkv=2, d=16)
+    _, logits, group, lall = oracle.verify(case.q, case.k_cache, case.v_cache, case.page_table,
+                                           case.prefix_len, case.gamma, case.scale, export="all")
+    s_all = oracle.aggregate(lall, case.prefix_len)
+    s_grp = oracle.aggregate(oracle.group_sums(lall, case.num_kv_heads), case.prefix_len)
+    G = case.num_q_heads // case.num_kv_heads
+    for b in range(case.batch):
+        P = int(case.prefix_len[b])
+        K = np.repeat(_logical(case, case.k_cache, b)[:P], G, axis=1)
+        coef = np.einsum("rhd,jhd->j", _f64(case.q[b]), K) * case.scale  # sum over rows and heads
+        assert np.max(np.abs(s_all[b, :P] - coef)) < 1e-10
+        assert np.max(np.abs(s_grp[b, :P] - coef)) < 1e-10
+        assert np.all(s_all[b, P:] == 0)
+
+
+def test_group_sums_match_the_c_export():
+    """oracle.group_sums over the two exported rows equals the C oracle's own group export."""
+    case = _tiny(prefix=(40, 17), gamma=4, hq=8, hkv=4, d=16)
+    _, logits, group, _ = oracle.verify(case.q, case.k_cache, case.v_cache, case.page_table,
+                                        case.prefix_len, case.gamma, case.scale)
+    assert np.max(np.abs(oracle.group_sums(logits, case.num_kv_heads) - group)) < 1e-12
+
+
+def test_two_row_collection_is_full_at_gamma_one():
+    """With gamma = 1 the first draft row and the bonus row are all the rows."""
+    case = _tiny(prefix=(30,), gamma=1, hq=4, hkv=2, d=16)
+    _, logits, group, lall = oracle.verify(case.q, case.k_cache, case.v_cache, case.page_table,
+                                           case.prefix_len, case.gamma, case.scale, export="all")
+    assert np.array_equal(logits, lall)
+    assert np.max(np.abs(oracle.group_sums(lall, case.num_kv_heads) - group)) < 1e-12

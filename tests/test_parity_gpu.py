@@ -300,3 +300,39 @@ def test_graph_replay_matches_eager(torch_cuda):
             assert np.array_equal(got["scores"][b, :P], ref["scores"][b, :P]), (rep, b)
             assert np.array_equal(got["sel_pos"][b, :k], ref["sel_pos"][b, :k]), (rep, b)
             assert np.array_equal(got["sel_slot"][b, :k], ref["sel_slot"][b, :k]), (rep, b)
+
+
+@pytest.mark.parametrize("name", ["c2_small", "c5_small", "short_prefixes", "gamma0"])
+def test_full_collection_parity(torch_cuda, name):
+    """All-rows export (the objective over every verify row): logits of every row,
+    group sums over every row, aggregation over gamma+1 rows, and the chain."""
+    import torch
+    from verification_guided_sparse_amd.runner import DeviceCase
+    c = synth.make_case(SMALL[name]())
+    _say(f"[parity] full collection {c.cfg.name}")
+    out_ref, _, _, lall = oracle.verify(c.q, c.k_cache, c.v_cache, c.page_table, c.prefix_len, c.gamma,
+                                        c.scale, export="all", nthreads=NTHREADS)
+    grp_ref = oracle.group_sums(lall, c.num_kv_heads)
+    dc = DeviceCase(c)
+    dc.verify(export="both", rows="all")
+    torch.cuda.synchronize()
+    _check(parity.output_gate(dc.host("out"), out_ref), "verify out")
+    _check(parity.score_gate(dc.host("logits_all"), lall, mask=_rows_mask(c, (c.rows, c.num_q_heads))),
+           "all-rows logits")
+    _check(parity.score_gate(dc.host("group"), grp_ref, mask=_rows_mask(c, (c.num_kv_heads,))),
+           "all-rows group sums")
+    # aggregation over gamma+1 rows, on the oracle's logits rounded to fp32
+    l32 = lall.astype(np.float32)
+    dc.put("logits_all", l32)
+    dc.aggregate(src="raw_all")
+    torch.cuda.synchronize()
+    s_ref = oracle.aggregate(l32.astype(np.float64), c.prefix_len)
+    _check(parity.score_gate(dc.host("scores"), s_ref, mask=_rows_mask(c, ())), "aggregate all rows")
+    # chain, both export forms
+    s_all = oracle.aggregate(lall, c.prefix_len)
+    for export in ("raw", "group"):
+        dc.iteration(export=export, rows="all")
+        torch.cuda.synchronize()
+        _check(parity.score_gate(dc.host("scores"), s_all, mask=_rows_mask(c, ())), f"chain[{export}] scores")
+        _check(parity.topk_gate(dc.host("sel_pos"), dc.host("sel_count"), s_all, c.prefix_len, c.k),
+               f"chain[{export}] topk")

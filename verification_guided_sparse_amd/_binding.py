@@ -31,7 +31,7 @@ VG_TOPK_PREPASS_DONE = 1
 # every symbol include/vegas_attn.h declares
 EXPORTS = (
     "vg_status_string", "vg_version", "vg_workspace_zero",
-    "vg_verify_workspace_size", "vg_verify_attention",
+    "vg_verify_workspace_size", "vg_verify_attention", "vg_verify_attention_all_rows",
     "vg_aggregate_scores",
     "vg_topk_workspace_size", "vg_topk_select",
     "vg_sparse_draft_workspace_size", "vg_sparse_draft_attention",
@@ -79,6 +79,7 @@ def lib():
         L.vg_workspace_zero.argtypes = [P, SZ, P]
         L.vg_verify_workspace_size.argtypes = [SP, I32, I32, C.POINTER(SZ)]
         L.vg_verify_attention.argtypes = [SP, P, P, P, P, P, I32, I32, P, P, P, P, SZ, P]
+        L.vg_verify_attention_all_rows.argtypes = [SP, P, P, P, P, P, I32, I32, P, P, P, P, SZ, P]
         L.vg_aggregate_scores.argtypes = [I32, P, I32, I32, P, I32, P, P, SZ, P]
         L.vg_topk_workspace_size.argtypes = [I32, I32, C.POINTER(SZ)]
         L.vg_topk_select.argtypes = [I32, P, I32, P, P, I32, P, I32, I32, P, P, P, I32, P, SZ, P]
@@ -141,6 +142,14 @@ def vg_verify_workspace_size(shape: VgShape, max_prefix: int, gamma: int) -> int
 def vg_verify_attention(shape, q, k_cache, v_cache, page_table, prefix_len, max_prefix, gamma, out,
                         logits, group_scores, workspace, workspace_bytes, stream=None):
     _check("vg_verify_attention", lib().vg_verify_attention(
+        C.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(prefix_len),
+        int(max_prefix), int(gamma), _ptr(out), _ptr(logits), _ptr(group_scores), _ptr(workspace),
+        int(workspace_bytes), _stream(stream)))
+
+
+def vg_verify_attention_all_rows(shape, q, k_cache, v_cache, page_table, prefix_len, max_prefix, gamma,
+                                 out, logits, group_scores, workspace, workspace_bytes, stream=None):
+    _check("vg_verify_attention_all_rows", lib().vg_verify_attention_all_rows(
         C.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(prefix_len),
         int(max_prefix), int(gamma), _ptr(out), _ptr(logits), _ptr(group_scores), _ptr(workspace),
         int(workspace_bytes), _stream(stream)))

@@ -151,8 +151,9 @@ struct WaveState {
   // per-lane constants of this lane's rows (row = rt*16 + i16)
   int vis_off[NT];       // the row sees entries i < s.vis0 + vis_off
   int head[NT];          // its query head, -1 for padding rows
-  float gw[NT];          // weight of the row in the group export: #{r in {0, gamma}}
-  int xrow[NT];          // export slots: bit 0 -> row 0 of the export, bit 1 -> row gamma
+  float gw[NT];          // weight of the row in the group export: #{r in {0, gamma}} (every row: 1)
+  int xrow[NT];          // export slots: bit x -> slot xbase + x of the raw export
+  int xbase[NT];         // 0, or the row r when every row is exported
 };
 
 template <int D, int NT>
@@ -197,7 +198,8 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
       st[tt][rt] = acc;
     }
 
-  // Logit export (verify): rows 0 and gamma, entries below the prefix length.
+  // Logit export (verify): rows 0 and gamma (or every row), entries below the
+  // prefix length.
   if (do_export && e0 < s.p_export) {
     if (a.logits) {
 #pragma unroll
@@ -207,7 +209,8 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
             if (W.xrow[rt] & (1 << x)) {
-              float *dst = a.logits + ((size_t)(b * 2 + x) * Hq + h) * a.max_prefix;
+              const int n_slots = a.export_all ? a.nrows : 2;
+              float *dst = a.logits + ((size_t)(b * n_slots + W.xbase[rt] + x) * Hq + h) * a.max_prefix;
 #pragma unroll
               for (int tt = 0; tt < 2; ++tt) {
                 const int e = e0 + tt * 16 + 4 * q4;
@@ -419,8 +422,15 @@ void attn_mfma_kernel(AttnArgs a_in) {
       const int r = row / G;
       W.vis_off[rt] = r;
       W.head[rt] = row < M ? g * G + row % G : -1;
-      W.gw[rt] = row < M ? (float)((r == 0) + (r == a.gamma)) : 0.f;
-      W.xrow[rt] = row < M ? ((r == 0) | ((r == a.gamma) << 1)) : 0;
+      if (a.export_all) {
+        W.gw[rt] = row < M ? 1.f : 0.f;
+        W.xrow[rt] = row < M ? 1 : 0;
+        W.xbase[rt] = r;
+      } else {
+        W.gw[rt] = row < M ? (float)((r == 0) + (r == a.gamma)) : 0.f;
+        W.xrow[rt] = row < M ? ((r == 0) | ((r == a.gamma) << 1)) : 0;
+        W.xbase[rt] = 0;
+      }
 #pragma unroll
       for (int at = 0; at < DPL; ++at) W.o[rt][at] = f32x4{0.f, 0.f, 0.f, 0.f};
     }

@@ -143,11 +143,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_valu_kernel(AttnArgs a) {
           if (m < M) {
             const int r = m / G, h = g * G + m % G;
             const float l = acc[m] * a.scale;
-            if (e < s.p_export) {
-              if (a.logits && r == 0) a.logits[((size_t)(b * 2 + 0) * Hq + h) * a.max_prefix + e] = l;
-              if (a.logits && r == a.gamma) a.logits[((size_t)(b * 2 + 1) * Hq + h) * a.max_prefix + e] = l;
+            if (e < s.p_export && a.logits) {
+              if (a.export_all) {
+                a.logits[((size_t)(b * a.nrows + r) * Hq + h) * a.max_prefix + e] = l;
+              } else {
+                if (r == 0) a.logits[((size_t)(b * 2 + 0) * Hq + h) * a.max_prefix + e] = l;
+                if (r == a.gamma) a.logits[((size_t)(b * 2 + 1) * Hq + h) * a.max_prefix + e] = l;
+              }
             }
-            gs += (float)((r == 0) + (r == a.gamma)) * acc[m];
+            gs += (a.export_all ? 1.f : (float)((r == 0) + (r == a.gamma))) * acc[m];
           }
         }
         if (a.group && e < s.p_export) a.group[(size_t)(b * Hkv + g) * a.max_prefix + e] = gs * a.scale;

@@ -211,6 +211,50 @@ SelWs sel_ws(const SelPlan &p, void *ws) {
 
 constexpr int kMaxSelectPrefix = kMaxChunks * kChunk;
 
+vg_status verify_impl(const vg_shape *shape, const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *page_table, const int32_t *prefix_len, int32_t max_prefix,
+                      int32_t gamma, float *out, float *logits, float *group_scores, void *workspace,
+                      size_t workspace_bytes, void *stream, bool export_all) {
+  if (!valid_shape(shape) || max_prefix < 0 || gamma < 0 || gamma > 15) return VG_ERR_INVALID_ARG;
+  const void *req[] = {q, k_cache, v_cache, page_table, prefix_len, out};
+  for (const void *p : req)
+    if (!p || !aligned16(p)) return VG_ERR_INVALID_ARG;
+  if ((logits && !aligned16(logits)) || (group_scores && !aligned16(group_scores)))
+    return VG_ERR_INVALID_ARG;
+  const vg_status sup = supported_shape(shape);
+  if (sup != VG_OK) return sup;
+  const int R = gamma + 1;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  if (R * G > kMaxRows) return VG_ERR_UNSUPPORTED;
+  if (ceil_div((long long)max_prefix + R, shape->page_size) > shape->max_pages_per_seq)
+    return VG_ERR_INVALID_ARG;
+  const AttnPlan p = plan_attention(shape, R, (long long)max_prefix + R, false);
+  if (!p.ok) return VG_ERR_UNSUPPORTED;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < p.bytes) return VG_ERR_WORKSPACE;
+  AttnArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.page_table = page_table;
+  a.prefix_len = prefix_len;
+  a.out = out;
+  a.logits = logits;
+  a.group = group_scores;
+  a.max_pages = shape->max_pages_per_seq;
+  a.max_prefix = max_prefix;
+  a.nrows = R;
+  a.gamma = gamma;
+  a.num_q_heads = shape->num_q_heads;
+  a.num_kv_heads = shape->num_kv_heads;
+  a.group_size = G;
+  a.scale = effective_scale(shape);
+  a.scale_log2 = a.scale * kLog2e;
+  a.sparse = 0;
+  a.export_all = export_all ? 1 : 0;
+  return launch_attention(shape, p, a, static_cast<char *>(workspace),
+                          static_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -258,43 +302,17 @@ vg_status vg_verify_attention(const vg_shape *shape, const void *q, const void *
                               const int32_t *prefix_len, int32_t max_prefix, int32_t gamma,
                               float *out, float *logits, float *group_scores, void *workspace,
                               size_t workspace_bytes, void *stream) {
-  if (!valid_shape(shape) || max_prefix < 0 || gamma < 0 || gamma > 15) return VG_ERR_INVALID_ARG;
-  const void *req[] = {q, k_cache, v_cache, page_table, prefix_len, out};
-  for (const void *p : req)
-    if (!p || !aligned16(p)) return VG_ERR_INVALID_ARG;
-  if ((logits && !aligned16(logits)) || (group_scores && !aligned16(group_scores)))
-    return VG_ERR_INVALID_ARG;
-  const vg_status sup = supported_shape(shape);
-  if (sup != VG_OK) return sup;
-  const int R = gamma + 1;
-  const int G = shape->num_q_heads / shape->num_kv_heads;
-  if (R * G > kMaxRows) return VG_ERR_UNSUPPORTED;
-  if (ceil_div((long long)max_prefix + R, shape->page_size) > shape->max_pages_per_seq)
-    return VG_ERR_INVALID_ARG;
-  const AttnPlan p = plan_attention(shape, R, (long long)max_prefix + R, false);
-  if (!p.ok) return VG_ERR_UNSUPPORTED;
-  if (!workspace || !aligned16(workspace) || workspace_bytes < p.bytes) return VG_ERR_WORKSPACE;
-  AttnArgs a{};
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.page_table = page_table;
-  a.prefix_len = prefix_len;
-  a.out = out;
-  a.logits = logits;
-  a.group = group_scores;
-  a.max_pages = shape->max_pages_per_seq;
-  a.max_prefix = max_prefix;
-  a.nrows = R;
-  a.gamma = gamma;
-  a.num_q_heads = shape->num_q_heads;
-  a.num_kv_heads = shape->num_kv_heads;
-  a.group_size = G;
-  a.scale = effective_scale(shape);
-  a.scale_log2 = a.scale * kLog2e;
-  a.sparse = 0;
-  return launch_attention(shape, p, a, static_cast<char *>(workspace),
-                          static_cast<hipStream_t>(stream));
+  return verify_impl(shape, q, k_cache, v_cache, page_table, prefix_len, max_prefix, gamma, out, logits,
+                     group_scores, workspace, workspace_bytes, stream, false);
+}
+
+vg_status vg_verify_attention_all_rows(const vg_shape *shape, const void *q, const void *k_cache,
+                                       const void *v_cache, const int32_t *page_table,
+                                       const int32_t *prefix_len, int32_t max_prefix, int32_t gamma,
+                                       float *out, float *logits, float *group_scores,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+  return verify_impl(shape, q, k_cache, v_cache, page_table, prefix_len, max_prefix, gamma, out, logits,
+                     group_scores, workspace, workspace_bytes, stream, true);
 }
 
 vg_status vg_aggregate_scores(int32_t batch, const float *src, int32_t src_rows, int32_t src_heads,

@@ -130,7 +130,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 //   entries [cnt_b, L_b)  are positions base_b + (i - cnt_b) translated through
 //                         the page table (verify: the whole cache; sparse: the tail).
 // Query row r (of nrows) sees entries i < L_b - nrows + 1 + r.
-// Verify additionally exports the logits of rows 0 and gamma for entries i < P_b.
+// Verify additionally exports the logits of rows 0 and gamma (or of every row)
+// for entries i < P_b.
 struct AttnArgs {
   const void *q;            // [B][nrows][Hq][D]
   const void *k_cache;      // [slots][Hkv][D]
@@ -142,7 +143,7 @@ struct AttnArgs {
   const int32_t *tail_start;  // [B] (sparse) or null
   const int32_t *tail_len;    // [B] (sparse) or null
   float *out;               // [B][nrows][Hq][D]
-  float *logits;            // [B][2][Hq][max_prefix] or null
+  float *logits;            // [B][2][Hq][max_prefix] (all rows: [B][nrows][Hq][max_prefix]) or null
   float *group;             // [B][Hkv][max_prefix] or null
   float *part_o;            // [parts][M][D], parts = workgroups + B * Hkv
   float *part_ml;           // [parts][M][2]
@@ -153,6 +154,7 @@ struct AttnArgs {
   int32_t tile;             // entries per tile of the attention kernel
   int32_t split_tokens;     // > 0: fixed splits of this many entries (see attn_common.h)
   int32_t splits;           // splits per (sequence, KV head) when split_tokens > 0
+  int32_t export_all;       // 0: rows 0 and gamma exported (Collect-2-Query); 1: every row
   float scale;       // logit = scale * q.k (natural-log units)
   float scale_log2;  // scale * log2(e)
   int32_t sparse;

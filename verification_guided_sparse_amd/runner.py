@@ -80,16 +80,31 @@ class DeviceCase:
         return ws
 
     # ------------------------------------------------------------------ steps
-    def verify(self, export="both", stream=None):
-        logits = self.logits if export in ("raw", "both") else None
+    @property
+    def logits_all(self):
+        """Every verify row's logits [B][R][Hq][max_prefix] (full collection), allocated on first use."""
+        if getattr(self, "_logits_all", None) is None:
+            self._logits_all = torch.zeros(self.B, self.R, self.Hq, self.max_prefix, dtype=torch.float32,
+                                           device=self.device)
+        return self._logits_all
+
+    def verify(self, export="both", rows="two", stream=None):
+        """export: "raw", "group", "both" or "none"; rows: "two" (Collect-2-Query: rows 0
+        and gamma into `logits`) or "all" (every row into `logits_all`; `group` then sums
+        all rows)."""
+        raw = self.logits if rows == "two" else self.logits_all
+        logits = raw if export in ("raw", "both") else None
         group = self.group if export in ("group", "both") else None
-        vg.vg_verify_attention(self.shape, self.q, self.k_cache, self.v_cache, self.page_table,
-                               self.prefix_len, self.max_prefix, self.gamma, self.out, logits, group,
-                               self.ws_verify, self.ws_verify_bytes, stream)
+        fn = vg.vg_verify_attention if rows == "two" else vg.vg_verify_attention_all_rows
+        fn(self.shape, self.q, self.k_cache, self.v_cache, self.page_table, self.prefix_len, self.max_prefix,
+           self.gamma, self.out, logits, group, self.ws_verify, self.ws_verify_bytes, stream)
 
     def aggregate(self, src="raw", fuse_prepass=False, stream=None):
+        """src: "raw" (two rows), "raw_all" (every row) or "group"."""
         if src == "raw":
             t, rows, heads = self.logits, 2, self.Hq
+        elif src == "raw_all":
+            t, rows, heads = self.logits_all, self.R, self.Hq
         else:
             t, rows, heads = self.group, 1, self.Hkv
         ws = self.ws_select if fuse_prepass else None
@@ -116,16 +131,17 @@ class DeviceCase:
             self.max_tail, self.draft_out if out is None else out,
             self.ws_sparse, self.ws_sparse_bytes, stream)
 
-    def iteration(self, export="group", stream=None):
+    def iteration(self, export="group", rows="two", stream=None):
         """One pass of the whole path: verify (+export), aggregate, top-k, gamma draft steps."""
-        self.verify(export=export, stream=stream)
-        self.aggregate(src="group" if export == "group" else "raw", fuse_prepass=True, stream=stream)
+        self.verify(export=export, rows=rows, stream=stream)
+        src = "group" if export == "group" else ("raw" if rows == "two" else "raw_all")
+        self.aggregate(src=src, fuse_prepass=True, stream=stream)
         self.topk(prepass_done=True, stream=stream)
         for s in range(self.gamma):
             self.sparse(step=s, stream=stream)
 
     # ------------------------------------------------------------- host copies
-    _PADDED = ("logits", "group", "scores")  # last dim padded past the case's max_prefix
+    _PADDED = ("logits", "logits_all", "group", "scores")  # last dim padded past the case's max_prefix
 
     def host(self, name):
         """Host copy of a device buffer (padded rows trimmed to the case's max_prefix)."""
