@@ -334,7 +334,11 @@ def breakdown(layers, c, export):
         "aggregate": lambda: [lc.aggregate(src=export, fuse_prepass=True) for lc in layers],
         "topk_after_prepass": lambda: [lc.topk(prepass_done=True) for lc in layers],
         "draft": lambda: [lc.sparse(step=c.gamma - 1) for lc in layers],
+        # rewrites the new tokens' own rows: the workload is unchanged
+        "kv_append": lambda: [lc.append() for lc in layers],
     }
+    for lc in layers:
+        lc.new_rows()  # allocated before capture
     out = {}
     for name, fn in kinds.items():
         if name == "topk_after_prepass":

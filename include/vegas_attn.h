@@ -243,6 +243,44 @@ vg_status vg_sparse_draft_attention(const vg_shape *shape, const void *q, int32_
                                     int32_t max_tail, float *out, void *workspace,
                                     size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------- KV append */
+
+/*
+ * Append the new tokens' K/V rows to the paged cache: the step before
+ * verification (the gamma+1 tokens verify attends to must already be cached;
+ * Vegas section 2, core mechanism), so that a whole iteration runs on the
+ * device.  For every sequence b, new token r in [0, n_new) and KV head g:
+ *     k_cache[slot(b, start_pos[b] + r)][g][:] = k_new[b][r][g][:]   (same for V)
+ * with slot(b, pos) = page_table[b][pos / 16] * 16 + pos % 16.  Copies are exact.
+ *
+ *   k_new, v_new  [B][n_new][Hkv][D] dtype (read)
+ *   page_table    [B][max_pages_per_seq] int32
+ *   start_pos     [B] int32: logical position of new token 0 (P_b for verify)
+ *   k_cache, v_cache [num_slots][Hkv][D] dtype (written at the new tokens' slots only)
+ *   n_new         0 <= n_new <= 65535 (0: nothing launched)
+ * Positions whose page-table entry is outside the row or negative are skipped.
+ * Supported: D in {64, 128}; page_size 16; f32 or bf16.
+ */
+vg_status vg_kv_append(const vg_shape *shape, const void *k_new, const void *v_new, int32_t n_new,
+                       const int32_t *page_table, const int32_t *start_pos, void *k_cache, void *v_cache,
+                       void *stream);
+
+/*
+ * Tail bookkeeping between iterations.  Of an iteration's gamma + 1 new tokens
+ * the sequence keeps the first (the token carried over from the previous
+ * iteration) and the n_accepted[b] draft tokens that verification accepted;
+ * the rejected drafts' slots are overwritten by the next append (Vegas
+ * section 2: drafts are accepted or rejected by verification):
+ *     prefix_len[b] += 1 + min(max(n_accepted[b], 0), gamma)
+ *
+ *   n_accepted  [B] int32 device (read)
+ *   prefix_len  [B] int32 device (updated in place)
+ * Pages for the grown sequences must already be in the page table (page
+ * allocation is the caller's).  batch = 0 launches nothing.
+ */
+vg_status vg_advance_prefix(int32_t batch, int32_t gamma, const int32_t *n_accepted, int32_t *prefix_len,
+                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

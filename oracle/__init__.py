@@ -90,6 +90,35 @@ def verify(q, k_cache, v_cache, page_table, prefix_len, gamma, scale, *, page_si
     return out, logits, group, lall
 
 
+def kv_append(k_cache, v_cache, k_new, v_new, page_table, start_pos, page_size=16):
+    """Copies of the caches with the new tokens' rows written at their slots:
+    cache[page_table[b][p // ps] * ps + p % ps] = new[b][r] for p = start_pos[b] + r
+    (the append that precedes verification: verify attends to the gamma + 1 new
+    tokens from the cache, Vegas section 2, core mechanism).  Positions whose
+    page-table entry lies outside the row or is negative are skipped."""
+    k = np.array(k_cache, copy=True)
+    v = np.array(v_cache, copy=True)
+    B, n_new = k_new.shape[:2]
+    max_pages = page_table.shape[1]
+    for b in range(B):
+        for r in range(n_new):
+            p = int(start_pos[b]) + r
+            if p < 0 or p // page_size >= max_pages or page_table[b][p // page_size] < 0:
+                continue
+            slot = int(page_table[b][p // page_size]) * page_size + p % page_size
+            k[slot] = k_new[b, r]
+            v[slot] = v_new[b, r]
+    return k, v
+
+
+def advance_prefix(prefix_len, n_accepted, gamma):
+    """Prefix lengths after an iteration: the sequence keeps its first new token
+    and the n accepted drafts (clamped to [0, gamma]) of the gamma + 1 tokens
+    verification judged (Vegas section 2, core mechanism)."""
+    return np.array([int(p) + 1 + min(max(int(n), 0), int(gamma)) for p, n in zip(prefix_len, n_accepted)],
+                    dtype=np.int32)
+
+
 def group_sums(src, num_kv_heads):
     """Group form of an export [B][T][Hq][max_prefix]: the sum over its T rows and
     the G = Hq / Hkv consecutive query heads of each KV head -> [B][Hkv][max_prefix]

@@ -371,3 +371,64 @@ def test_two_row_collection_is_full_at_gamma_one():
                                            case.prefix_len, case.gamma, case.scale, export="all")
     assert np.array_equal(logits, lall)
     assert np.max(np.abs(oracle.group_sums(lall, case.num_kv_heads) - group)) < 1e-12
+
+
+def test_kv_append_rebuilds_the_cache():
+    """Writing each sequence's new tokens (read back through the page table) into a
+    cache whose new-token slots were cleared reproduces the cache exactly."""
+    case = _tiny(prefix=(37, 5, 20), gamma=3, hq=4, hkv=2, d=16, paging="permuted")
+    R = case.rows
+
+    def raw_rows(cache, b):  # the stored rows (raw bits) of positions P_b .. P_b + gamma
+        pos = np.arange(int(case.prefix_len[b]), int(case.prefix_len[b]) + R)
+        return cache[case.page_table[b, pos // 16].astype(np.int64) * 16 + pos % 16]
+
+    k_new = np.stack([raw_rows(case.k_cache, b) for b in range(case.batch)])
+    v_new = np.stack([raw_rows(case.v_cache, b) for b in range(case.batch)])
+    k0, v0 = case.k_cache.copy(), case.v_cache.copy()
+    for b in range(case.batch):
+        for r in range(R):
+            p = int(case.prefix_len[b]) + r
+            slot = int(case.page_table[b][p // 16]) * 16 + p % 16
+            k0[slot] = 0
+            v0[slot] = 0
+    assert not np.array_equal(k0, case.k_cache)
+    k1, v1 = oracle.kv_append(k0, v0, k_new, v_new, case.page_table, case.prefix_len)
+    assert np.array_equal(k1, case.k_cache) and np.array_equal(v1, case.v_cache)
+
+
+def test_iterations_grow_the_logical_sequence():
+    """Append the new tokens, keep the first and the accepted drafts, repeat: each
+    sequence read back in position order through its page table is the starting
+    prefix followed, per iteration, by the first new token and the accepted drafts
+    (the rejected drafts' slots are overwritten by the next append)."""
+    case = _tiny(prefix=(37, 21, 30), gamma=3, hq=4, hkv=2, d=16, paging="permuted")
+    R, n_iter = case.rows, 2
+    p = (case.prefix_len - n_iter * R).astype(np.int32)  # the pages cover prefix_len + R
+    assert (p > 0).all()
+    k, v = case.k_cache.copy(), case.v_cache.copy()
+
+    def logical(cache, b, n):
+        pos = np.arange(n)
+        return cache[case.page_table[b, pos // 16].astype(np.int64) * 16 + pos % 16]
+
+    want_k = [list(logical(k, b, int(p[b]))) for b in range(case.batch)]
+    want_v = [list(logical(v, b, int(p[b]))) for b in range(case.batch)]
+    for it in range(n_iter):
+        k_new, v_new = synth.new_token_rows(case, it)
+        k, v = oracle.kv_append(k, v, k_new, v_new, case.page_table, p)
+        n = synth.accepted_counts(case, it)
+        assert ((n >= 0) & (n <= case.gamma)).all()
+        p = oracle.advance_prefix(p, n, case.gamma)
+        for b in range(case.batch):
+            want_k[b] += list(k_new[b, : 1 + n[b]])
+            want_v[b] += list(v_new[b, : 1 + n[b]])
+    for b in range(case.batch):
+        assert len(want_k[b]) == p[b]
+        assert np.array_equal(logical(k, b, int(p[b])), np.stack(want_k[b]))
+        assert np.array_equal(logical(v, b, int(p[b])), np.stack(want_v[b]))
+    # counts outside [0, gamma] are clamped; writes past the page-table row are skipped
+    assert list(oracle.advance_prefix([10, 10, 10], [-3, 2, 99], 3)) == [11, 13, 14]
+    far = np.full(case.batch, case.page_table.shape[1] * 16, np.int32)
+    k2, _ = oracle.kv_append(k, v, k_new, v_new, case.page_table, far)
+    assert np.array_equal(k2, k)

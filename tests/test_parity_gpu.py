@@ -159,6 +159,8 @@ SMALL = {
     # 64 query rows per KV head at D = 128 (4 row tiles)
     "rows64_d128": lambda: synth.small("c2_qwen3_32k", prefix=(2100,), num_q_heads=64, num_kv_heads=8,
                                        gamma=7),
+    # empty prefixes (P = 0): the new tokens only, nothing to export or select
+    "empty_prefix": lambda: synth.small("c2_qwen3_32k", prefix=(0, 3000, 0, 40), gamma=4, k_pct=50),
     # k = P: every prefix position selected
     "k_all": lambda: synth.small("c5_gptoss_64k", prefix=(300, 77), k_pct=100),
 }
@@ -336,3 +338,98 @@ def test_full_collection_parity(torch_cuda, name):
         _check(parity.score_gate(dc.host("scores"), s_all, mask=_rows_mask(c, ())), f"chain[{export}] scores")
         _check(parity.topk_gate(dc.host("sel_pos"), dc.host("sel_count"), s_all, c.prefix_len, c.k),
                f"chain[{export}] topk")
+
+
+@pytest.mark.parametrize("name", ["c4_small", "c1_tiny", "c5_small"])
+def test_kv_append_bit_exact(torch_cuda, name):
+    """The new tokens' rows written into a cache whose new-token slots were cleared:
+    bit-identical to the oracle's append (and to the generated cache); positions
+    outside the page-table row are skipped; the chain then verifies as usual."""
+    import torch
+    from verification_guided_sparse_amd import _binding as vg
+    from verification_guided_sparse_amd.runner import DeviceCase, _dev
+    c = synth.make_case(SMALL[name]())
+    R = c.rows
+    pos = [np.arange(int(c.prefix_len[b]), int(c.prefix_len[b]) + R) for b in range(c.batch)]
+    slots = [c.page_table[b, p // 16].astype(np.int64) * 16 + p % 16 for b, p in enumerate(pos)]
+    k_new = np.stack([c.k_cache[s] for s in slots])  # [B][R][Hkv][D] raw
+    v_new = np.stack([c.v_cache[s] for s in slots])
+    k0, v0 = c.k_cache.copy(), c.v_cache.copy()
+    for s in slots:
+        k0[s] = 0
+        v0[s] = 0
+    k_ref, v_ref = oracle.kv_append(k0, v0, k_new, v_new, c.page_table, c.prefix_len)
+    assert np.array_equal(k_ref, c.k_cache) and np.array_equal(v_ref, c.v_cache)
+    _say(f"[parity] kv append {c.cfg.name}")
+    dc = DeviceCase(c)
+    # raw element bits both ways (bf16 travels as int16; the host side is uint16)
+    up = lambda a: _dev(a, "cuda")
+    down = lambda t, like: t.cpu().numpy().view(like.dtype)
+    dc.k_cache.copy_(up(k0))
+    dc.v_cache.copy_(up(v0))
+    tk, tv = up(k_new), up(v_new)
+    vg.vg_kv_append(dc.shape, tk, tv, R, dc.page_table, dc.prefix_len, dc.k_cache, dc.v_cache)
+    torch.cuda.synchronize()
+    assert np.array_equal(down(dc.k_cache, k_ref), k_ref)
+    assert np.array_equal(down(dc.v_cache, v_ref), v_ref)
+    # start positions past every page-table row: nothing is written
+    far = torch.full_like(dc.prefix_len, dc.max_pages * 16)
+    vg.vg_kv_append(dc.shape, tk, tv, R, dc.page_table, far, dc.k_cache, dc.v_cache)
+    torch.cuda.synchronize()
+    assert np.array_equal(down(dc.k_cache, k_ref), k_ref)
+    # the appended cache verifies like the generated one
+    out_ref, _, group_ref = _oracle_all(c)
+    dc.verify(export="group")
+    torch.cuda.synchronize()
+    _check(parity.output_gate(dc.host("out"), out_ref), "verify after append")
+    _check(parity.score_gate(dc.host("group"), group_ref, mask=_rows_mask(c, (c.num_kv_heads,))),
+           "group after append")
+
+
+@pytest.mark.parametrize("name", ["c4_small", "c5_small", "short_prefixes"])
+def test_iterations_on_device(torch_cuda, name):
+    """Several iterations with the cache, the prefix lengths and the selection kept on
+    the device: append the new tokens, verify (group export), aggregate, top-k, the
+    draft steps, then keep the accepted tokens.  Each iteration against the oracle run
+    on a host copy of the same state; the cache and the lengths bit-exact."""
+    import torch
+    from verification_guided_sparse_amd.runner import DeviceCase, _dev
+    c = synth.make_case(SMALL[name]())
+    R, n_iter = c.rows, 3
+    p = (c.prefix_len - n_iter * R).astype(np.int32)  # the pages cover prefix_len + R
+    p = np.maximum(p, 0)
+    _say(f"[parity] iterations {c.cfg.name} start P={list(p)} gamma={c.gamma}")
+    dc = DeviceCase(c)
+    dc.prefix_len.copy_(torch.from_numpy(p))
+    k_host, v_host = c.k_cache.copy(), c.v_cache.copy()
+    down = lambda t, like: t.cpu().numpy().view(like.dtype)
+    for it in range(n_iter):
+        k_new, v_new = synth.new_token_rows(c, it)
+        dc.append(_dev(k_new, "cuda"), _dev(v_new, "cuda"))
+        k_host, v_host = oracle.kv_append(k_host, v_host, k_new, v_new, c.page_table, p)
+        dc.verify(export="group")
+        dc.aggregate(src="group", fuse_prepass=True)
+        dc.topk(prepass_done=True)
+        dc.sparse(step=c.gamma - 1, tail_start=dc.prefix_len) if c.gamma else None
+        torch.cuda.synchronize()
+        out_ref, _, group_ref, _ = oracle.verify(c.q, k_host, v_host, c.page_table, p, c.gamma, c.scale,
+                                                 max_prefix=c.max_prefix, nthreads=NTHREADS)
+        what = f"iteration {it}"
+        _check(parity.output_gate(dc.host("out"), out_ref), f"{what} verify out")
+        _check(parity.score_gate(dc.host("group"), group_ref,
+                                 mask=parity.prefix_mask(p, c.max_prefix, (c.num_kv_heads,))), f"{what} group")
+        s_ref = oracle.aggregate(group_ref, p)
+        pos, cnt = dc.host("sel_pos"), dc.host("sel_count")
+        _check(parity.topk_gate(pos, cnt, s_ref, p, c.k), f"{what} topk")
+        if c.gamma:
+            s = c.gamma - 1
+            o_ref = oracle.sparse(np.ascontiguousarray(c.q_draft[s][:, None]), k_host, v_host, c.page_table,
+                                  pos, cnt, p, np.full(c.batch, s + 1, np.int32), c.scale, nthreads=NTHREADS)
+            _check(parity.output_gate(dc.host("draft_out"), o_ref), f"{what} sparse draft")
+        n = synth.accepted_counts(c, it)
+        dc.advance(_dev(n, "cuda"))
+        p = oracle.advance_prefix(p, n, c.gamma)
+        torch.cuda.synchronize()
+        _check(parity.exact_gate(dc.host("prefix_len"), p), f"{what} prefix lengths")
+    assert np.array_equal(down(dc.k_cache, k_host), k_host)
+    assert np.array_equal(down(dc.v_cache, v_host), v_host)

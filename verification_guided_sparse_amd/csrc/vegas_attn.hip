@@ -13,6 +13,7 @@
 #include "attn_mfma.h"
 #include "attn_valu.h"
 #include "select.h"
+#include "kv_append.h"
 
 namespace {
 
@@ -447,6 +448,42 @@ vg_status vg_sparse_draft_attention(const vg_shape *shape, const void *q, int32_
   a.sparse = 1;
   return launch_attention(shape, p, a, static_cast<char *>(workspace),
                           static_cast<hipStream_t>(stream));
+}
+
+vg_status vg_kv_append(const vg_shape *shape, const void *k_new, const void *v_new, int32_t n_new,
+                       const int32_t *page_table, const int32_t *start_pos, void *k_cache, void *v_cache,
+                       void *stream) {
+  if (!valid_shape(shape) || n_new < 0) return VG_ERR_INVALID_ARG;
+  const void *req[] = {k_new, v_new, page_table, start_pos, k_cache, v_cache};
+  for (const void *p : req)
+    if (!p || !aligned16(p)) return VG_ERR_INVALID_ARG;
+  const vg_status sup = supported_shape(shape);
+  if (sup != VG_OK) return sup;
+  if (n_new == 0) return VG_OK;
+  if (n_new > 65535 || shape->batch > 65535) return VG_ERR_UNSUPPORTED;
+  AppendArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.page_table = page_table;
+  a.start_pos = start_pos;
+  a.n_new = n_new;
+  a.max_pages = shape->max_pages_per_seq;
+  const int elem = shape->dtype == VG_DTYPE_BF16 ? 2 : 4;
+  a.row_vec16 = shape->num_kv_heads * shape->head_dim * elem / 16;
+  hipLaunchKernelGGL(kv_append_kernel, dim3(n_new, shape->batch), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
+}
+
+vg_status vg_advance_prefix(int32_t batch, int32_t gamma, const int32_t *n_accepted, int32_t *prefix_len,
+                            void *stream) {
+  if (batch < 0 || gamma < 0 || (batch > 0 && (!n_accepted || !prefix_len))) return VG_ERR_INVALID_ARG;
+  if (batch == 0) return VG_OK;
+  hipLaunchKernelGGL(advance_prefix_kernel, dim3((batch + 255) / 256), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), batch, gamma, n_accepted, prefix_len);
+  return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
 }
 
 }  // extern "C"

@@ -131,6 +131,30 @@ class DeviceCase:
             self.max_tail, self.draft_out if out is None else out,
             self.ws_sparse, self.ws_sparse_bytes, stream)
 
+    def new_rows(self):
+        """The R new tokens' K/V rows [B][R][Hkv][D] as generated (copies of their
+        cache rows), on the device: an append of these rewrites the same values."""
+        if getattr(self, "_new_rows", None) is None:
+            c, ps = self.case, self.case.page_size
+            p = c.prefix_len.astype(np.int64)[:, None] + np.arange(self.R)
+            slot = c.page_table[np.arange(self.B)[:, None], p // ps].astype(np.int64) * ps + p % ps
+            idx = torch.from_numpy(slot.reshape(-1)).to(self.device)
+            shp = (self.B, self.R, self.Hkv, self.D)
+            self._new_rows = (self.k_cache[idx].reshape(shp).contiguous(),
+                              self.v_cache[idx].reshape(shp).contiguous())
+        return self._new_rows
+
+    def append(self, k_new=None, v_new=None, start_pos=None, stream=None):
+        """Write the new tokens' rows at positions start_pos[b] + r (default: prefix_len)."""
+        if k_new is None:
+            k_new, v_new = self.new_rows()
+        vg.vg_kv_append(self.shape, k_new, v_new, k_new.shape[1], self.page_table,
+                        self.prefix_len if start_pos is None else start_pos, self.k_cache, self.v_cache, stream)
+
+    def advance(self, n_accepted, stream=None):
+        """Keep the first new token and the accepted drafts: prefix_len += 1 + n."""
+        vg.vg_advance_prefix(self.B, self.gamma, n_accepted, self.prefix_len, stream)
+
     def iteration(self, export="group", rows="two", stream=None):
         """One pass of the whole path: verify (+export), aggregate, top-k, gamma draft steps."""
         self.verify(export=export, rows=rows, stream=stream)

@@ -189,6 +189,8 @@ def _unit_vectors(seed: int, b: int, hkv: int, d: int) -> np.ndarray:
 
 def _heavy_positions(cfg: Config, seed: int, b: int, p: int) -> np.ndarray:
     """Sorted heavy-hitter positions in [1, p): `spans` clustered runs plus scattered ones."""
+    if p == 0:
+        return np.zeros(0, dtype=np.int64)
     n_hh = pct_round_half_up(p, cfg.hh_pct)
     g = _rng(seed, (4, b))
     taken = np.zeros(p, dtype=bool)
@@ -291,6 +293,21 @@ def make_case(cfg: Config | str, seed: int | None = None) -> Case:
                 dtype=cfg.dtype, gamma=cfg.gamma, page_size=ps, scale=scale, q=q,
                 q_draft=q_draft, k_cache=k_cache, v_cache=v_cache, page_table=page_table,
                 prefix_len=prefix, k=k, heavy=heavy)
+
+
+def new_token_rows(case: Case, it: int) -> tuple[np.ndarray, np.ndarray]:
+    """Seeded K/V rows of one iteration's gamma + 1 new tokens, [B][R][Hkv][D] in the
+    case's storage dtype (same scale as the cache, no heavy-hitter terms)."""
+    B, R, Hkv, D = case.batch, case.rows, case.num_kv_heads, case.head_dim
+    n = B * R * Hkv * D
+    k = _normal(case.cfg.seed, (30, it), n, case.cfg.sigma).reshape(B, R, Hkv, D)
+    v = _normal(case.cfg.seed, (31, it), n, case.cfg.sigma).reshape(B, R, Hkv, D)
+    return _store(k, case.dtype), _store(v, case.dtype)
+
+
+def accepted_counts(case: Case, it: int) -> np.ndarray:
+    """Seeded accepted-draft counts of one iteration, int32 [B] uniform in [0, gamma]."""
+    return _rng(case.cfg.seed, (32, it)).integers(0, case.gamma + 1, case.batch).astype(np.int32)
 
 
 def small(name: str, prefix=None, **kw) -> Config:
