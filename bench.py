@@ -336,6 +336,9 @@ def breakdown(layers, c, export):
         "draft": lambda: [lc.sparse(step=c.gamma - 1) for lc in layers],
         # rewrites the new tokens' own rows: the workload is unchanged
         "kv_append": lambda: [lc.append() for lc in layers],
+        # the query-agnostic baseline: sink + recent window, then a draft step over it
+        "window_select": lambda: [lc.window(n_sink=4) for lc in layers],
+        "draft_over_window": lambda: [lc.sparse(step=c.gamma - 1) for lc in layers],
     }
     for lc in layers:
         lc.new_rows()  # allocated before capture
@@ -360,6 +363,9 @@ def breakdown(layers, c, export):
     out = {k: round(v, 2) for k, v in out.items()}
     out["overhead_frac"] = round((out["verify"] - out["verify_no_export"] + out["aggregate"] + out["topk"])
                                  / out["verify_no_export"], 4)
+    g = max(c.gamma, 1)
+    out["iteration_vegas"] = round(out["verify"] + out["aggregate"] + out["topk"] + g * out["draft"], 2)
+    out["iteration_window"] = round(out["verify_no_export"] + out["window_select"] + g * out["draft_over_window"], 2)
     # restore a consistent selection for later replays
     for lc in layers:
         lc.iteration(export=export)

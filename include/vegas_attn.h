@@ -243,6 +243,30 @@ vg_status vg_sparse_draft_attention(const vg_shape *shape, const void *q, int32_
                                     int32_t max_tail, float *out, void *workspace,
                                     size_t workspace_bytes, void *stream);
 
+/*
+ * Query-agnostic selection (Vegas section 1: sliding-window style selection
+ * has little overhead but drafts less accurately; section 4 compares against
+ * such a streaming baseline): the first n_sink prefix positions (attention
+ * sinks) and the most recent ones, k_b positions in all, in the same output
+ * form as vg_topk_select, so that vg_sparse_draft_attention takes either list.
+ * With kk = min(k[b], P_b, max_k) and s = min(n_sink, kk):
+ *     sel_pos[b][0..kk) = 0, 1, ..., s-1, P_b-(kk-s), ..., P_b-1   (ascending)
+ *     sel_slot[b][i]    = page_table[b][pos / page_size] * page_size + pos % page_size
+ *     sel_count[b]      = kk
+ * Entries past kk are not written.  No scores are read.
+ *
+ *   prefix_len  [B] int32, 0 <= P_b <= max_prefix (clamped to that range)
+ *   k           [B] int32, 0 <= k[b] <= max_k (clamped)
+ *   n_sink      >= 0
+ *   page_table  [B][max_pages_per_seq] int32 (needed when sel_slot is non-null)
+ *   sel_pos     [B][max_k] int32;  sel_slot [B][max_k] int32 (nullable);  sel_count [B] int32
+ * 1 <= batch <= 65535.
+ */
+vg_status vg_window_select(int32_t batch, int32_t max_prefix, const int32_t *prefix_len, const int32_t *k,
+                           int32_t max_k, int32_t n_sink, const int32_t *page_table, int32_t page_size,
+                           int32_t max_pages_per_seq, int32_t *sel_pos, int32_t *sel_slot, int32_t *sel_count,
+                           void *stream);
+
 /* ------------------------------------------------------------- KV append */
 
 /*

@@ -111,6 +111,29 @@ def kv_append(k_cache, v_cache, k_new, v_new, page_table, start_pos, page_size=1
     return k, v
 
 
+def window_select(prefix_len, k, n_sink, page_table=None, page_size=16, max_k=None):
+    """Query-agnostic selection (the sliding-window style baseline of Vegas
+    section 1): the first min(n_sink, kk) prefix positions and the most recent
+    ones, kk = min(k_b, P_b) in all, ascending; with their page-size-1 slots.
+    Returns (pos [B][max_k], slot [B][max_k], count [B]), unwritten entries -1."""
+    B = len(prefix_len)
+    mk = max(1, int(max(k)) if max_k is None else int(max_k))
+    pos = np.full((B, mk), -1, dtype=np.int32)
+    slot = np.full((B, mk), -1, dtype=np.int32)
+    cnt = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        P = int(prefix_len[b])
+        kk = min(int(k[b]), P, mk)
+        chosen = sorted(set(range(min(n_sink, kk))) | set(range(P - (kk - min(n_sink, kk)), P)))
+        assert len(chosen) == kk
+        for i, j in enumerate(chosen):
+            pos[b, i] = j
+            if page_table is not None:
+                slot[b, i] = int(page_table[b][j // page_size]) * page_size + j % page_size
+        cnt[b] = kk
+    return pos, slot, cnt
+
+
 def advance_prefix(prefix_len, n_accepted, gamma):
     """Prefix lengths after an iteration: the sequence keeps its first new token
     and the n accepted drafts (clamped to [0, gamma]) of the gamma + 1 tokens

@@ -432,3 +432,23 @@ def test_iterations_grow_the_logical_sequence():
     far = np.full(case.batch, case.page_table.shape[1] * 16, np.int32)
     k2, _ = oracle.kv_append(k, v, k_new, v_new, case.page_table, far)
     assert np.array_equal(k2, k)
+
+
+@pytest.mark.parametrize("n_sink", [0, 1, 4, 16])
+def test_window_select_is_topk_of_a_recency_score(n_sink):
+    """The query-agnostic selection equals the exact top-k of a score that ranks
+    the sink positions above everything and the rest by recency (a special case
+    of the pinned top-k): same positions and slots, for k from 0 past P."""
+    case = _tiny(prefix=(37, 5, 20, 1), gamma=2, paging="permuted")
+    P = case.prefix_len
+    mp = int(P.max())
+    j = np.arange(mp, dtype=np.float64)
+    score = np.where(j < n_sink, 1e6, j)[None].repeat(len(P), 0)
+    for kv in (0, 1, 3, 4, 5, 17, 40):
+        k = np.full(len(P), kv, np.int32)
+        pos, slot, cnt = oracle.window_select(P, k, n_sink, case.page_table, max_k=max(kv, 1))
+        tp, ts, tc = oracle.topk(score, P, k, page_table=case.page_table, max_k=max(kv, 1))
+        assert np.array_equal(cnt, tc)
+        for b in range(len(P)):
+            n = int(cnt[b])
+            assert np.array_equal(pos[b, :n], tp[b, :n]) and np.array_equal(slot[b, :n], ts[b, :n]), (kv, b)

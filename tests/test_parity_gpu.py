@@ -433,3 +433,32 @@ def test_iterations_on_device(torch_cuda, name):
         _check(parity.exact_gate(dc.host("prefix_len"), p), f"{what} prefix lengths")
     assert np.array_equal(down(dc.k_cache, k_host), k_host)
     assert np.array_equal(down(dc.v_cache, v_host), v_host)
+
+
+@pytest.mark.parametrize("name", ["c4_small", "c5_small", "short_prefixes", "empty_prefix"])
+@pytest.mark.parametrize("n_sink", [0, 4])
+def test_window_select_and_draft(torch_cuda, name, n_sink):
+    """The query-agnostic selection, bit-exact against the oracle, then every draft
+    step through the same sparse kernel over it."""
+    import torch
+    from verification_guided_sparse_amd.runner import DeviceCase
+    c = synth.make_case(SMALL[name]())
+    _say(f"[parity] window select {c.cfg.name} n_sink={n_sink} k={list(c.k)}")
+    dc = DeviceCase(c)
+    dc.window(n_sink=n_sink)
+    torch.cuda.synchronize()
+    pos_ref, slot_ref, cnt_ref = oracle.window_select(c.prefix_len, c.k, n_sink, c.page_table, max_k=dc.max_k)
+    cnt = dc.host("sel_count")
+    _check(parity.exact_gate(cnt, cnt_ref), "window count")
+    pos, slot = dc.host("sel_pos"), dc.host("sel_slot")
+    for b in range(c.batch):
+        n = int(cnt_ref[b])
+        _check(parity.exact_gate(pos[b, :n], pos_ref[b, :n]), f"window positions seq {b}")
+        _check(parity.exact_gate(slot[b, :n], slot_ref[b, :n]), f"window slots seq {b}")
+    for s in range(c.gamma):
+        dc.sparse(step=s)
+        torch.cuda.synchronize()
+        o_ref = oracle.sparse(np.ascontiguousarray(c.q_draft[s][:, None]), c.k_cache, c.v_cache,
+                              c.page_table, pos_ref, cnt_ref, c.prefix_len,
+                              np.full(c.batch, s + 1, np.int32), c.scale, nthreads=NTHREADS)
+        _check(parity.output_gate(dc.host("draft_out"), o_ref), f"draft over the window, step {s}")

@@ -35,7 +35,7 @@ EXPORTS = (
     "vg_aggregate_scores",
     "vg_topk_workspace_size", "vg_topk_select",
     "vg_sparse_draft_workspace_size", "vg_sparse_draft_attention",
-    "vg_kv_append", "vg_advance_prefix",
+    "vg_window_select", "vg_kv_append", "vg_advance_prefix",
 )
 
 
@@ -86,6 +86,7 @@ def lib():
         L.vg_topk_select.argtypes = [I32, P, I32, P, P, I32, P, I32, I32, P, P, P, I32, P, SZ, P]
         L.vg_sparse_draft_workspace_size.argtypes = [SP, I32, I32, I32, C.POINTER(SZ)]
         L.vg_sparse_draft_attention.argtypes = [SP, P, I32, P, P, P, P, I32, P, P, P, I32, P, P, SZ, P]
+        L.vg_window_select.argtypes = [I32, I32, P, P, I32, I32, P, I32, I32, P, P, P, P]
         L.vg_kv_append.argtypes = [SP, P, P, I32, P, P, P, P, P]
         L.vg_advance_prefix.argtypes = [I32, I32, P, P, P]
         for name in EXPORTS[2:]:
@@ -194,6 +195,13 @@ def vg_sparse_draft_attention(shape, q, n_q, k_cache, v_cache, sel_slot, sel_cou
         C.byref(shape), _ptr(q), int(n_q), _ptr(k_cache), _ptr(v_cache), _ptr(sel_slot),
         _ptr(sel_count), int(max_k), _ptr(page_table), _ptr(tail_start), _ptr(tail_len),
         int(max_tail), _ptr(out), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def vg_window_select(batch, max_prefix, prefix_len, k, max_k, n_sink, page_table, page_size, max_pages,
+                     sel_pos, sel_slot, sel_count, stream=None):
+    _check("vg_window_select", lib().vg_window_select(
+        int(batch), int(max_prefix), _ptr(prefix_len), _ptr(k), int(max_k), int(n_sink), _ptr(page_table),
+        int(page_size), int(max_pages), _ptr(sel_pos), _ptr(sel_slot), _ptr(sel_count), _stream(stream)))
 
 
 def vg_kv_append(shape, k_new, v_new, n_new, page_table, start_pos, k_cache, v_cache, stream=None):

@@ -14,6 +14,7 @@
 #include "attn_valu.h"
 #include "select.h"
 #include "kv_append.h"
+#include "window_select.h"
 
 namespace {
 
@@ -474,6 +475,35 @@ vg_status vg_kv_append(const vg_shape *shape, const void *k_new, const void *v_n
   a.row_vec16 = shape->num_kv_heads * shape->head_dim * elem / 16;
   hipLaunchKernelGGL(kv_append_kernel, dim3(n_new, shape->batch), dim3(256), 0,
                      static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
+}
+
+vg_status vg_window_select(int32_t batch, int32_t max_prefix, const int32_t *prefix_len, const int32_t *k,
+                           int32_t max_k, int32_t n_sink, const int32_t *page_table, int32_t page_size,
+                           int32_t max_pages_per_seq, int32_t *sel_pos, int32_t *sel_slot, int32_t *sel_count,
+                           void *stream) {
+  if (batch < 1 || batch > 65535 || max_prefix < 0 || max_k < 0 || n_sink < 0) return VG_ERR_INVALID_ARG;
+  const void *req[] = {prefix_len, k, sel_pos, sel_count};
+  for (const void *p : req)
+    if (!p || !aligned16(p)) return VG_ERR_INVALID_ARG;
+  if (sel_slot && (!aligned16(sel_slot) || !page_table || !aligned16(page_table) ||
+                   page_size < 1 || max_pages_per_seq < 1 ||
+                   ceil_div(max_prefix, page_size) > max_pages_per_seq))
+    return VG_ERR_INVALID_ARG;
+  WindowArgs a{};
+  a.prefix_len = prefix_len;
+  a.k = k;
+  a.page_table = page_table;
+  a.sel_pos = sel_pos;
+  a.sel_slot = sel_slot;
+  a.sel_count = sel_count;
+  a.max_prefix = max_prefix;
+  a.max_k = max_k;
+  a.n_sink = n_sink;
+  a.page_size = page_size;
+  a.max_pages = max_pages_per_seq;
+  const int gx = std::max(1, std::min(ceil_div(max_k, 256), 64));
+  hipLaunchKernelGGL(window_select_kernel, dim3(gx, batch), dim3(256), 0, static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
 }
 

@@ -118,6 +118,13 @@ class DeviceCase:
                           self.max_pages, self.sel_pos, self.sel_slot, self.sel_count, flags,
                           self.ws_select, self.ws_select_bytes, stream)
 
+    def window(self, n_sink=4, stream=None):
+        """Query-agnostic selection into the same buffers as topk(): n_sink sink
+        positions plus the most recent ones, k_b in all."""
+        vg.vg_window_select(self.B, self.max_prefix, self.prefix_len, self.k, self.max_k, n_sink,
+                            self.page_table, self.case.page_size, self.max_pages, self.sel_pos,
+                            self.sel_slot, self.sel_count, stream)
+
     def sparse(self, step=0, q=None, sel_slot=None, sel_count=None, tail_start=None, tail_len=None,
                out=None, n_q=1, stream=None):
         qq = self.q_draft[step] if q is None else q
