@@ -111,6 +111,11 @@ def main():
     ap.add_argument("--collection", action="store_true",
                     help="also time the logit export + aggregation for two rows (Collect-2-Query) "
                          "against every row (full collection)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only run the kernel-cost sweep over the selection ratio x gamma "
+                         "(us per layer iteration at each point) for --workload")
+    ap.add_argument("--sweep-gammas", default="2,4,6,8")
+    ap.add_argument("--sweep-k-pcts", default="1,2,4,8,16")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (HBM byte-counter calibration)")
     args = ap.parse_args()
@@ -129,13 +134,15 @@ def main():
     from verification_guided_sparse_amd.runner import DeviceCase
 
     vg.lib()  # fail loudly if the HIP library is missing
+    if args.sweep:
+        sweep(args)
+        return
     kernel = {"auto": vg.VG_KERNEL_AUTO, "valu": vg.VG_KERNEL_VALU, "mfma": vg.VG_KERNEL_MFMA}[args.kernel]
     c = synth.make_case(args.workload)
     ab = algorithmic_bytes(c, args.export)
-    layer_kv = int((c.prefix_len.astype(np.int64) + c.rows).sum()) * c.num_kv_heads * c.head_dim * 2 * (
-        2 if c.dtype == "bf16" else 4)
-    L = args.layers or max(2, int(np.ceil(3 * 256e6 / max(sum(ab["draft"]) / max(c.gamma, 1), 1))))
-    L = min(L, 64, max(2, int(40e9 // layer_kv)))
+    L, layer_kv = layer_count(c, ab)
+    if args.layers:
+        L = args.layers
     print(f"[bench] {args.workload}: {L} layers, {layer_kv / 1e6:.1f} MB KV per layer, "
           f"export={args.export}, kernel={args.kernel}", file=sys.stderr, flush=True)
 
@@ -321,6 +328,68 @@ def collection(layers):
     out["overhead_group_two"] = round(t["verify_group_two"] - base + t["aggregate_group"], 2)
     out["overhead_group_all"] = round(t["verify_group_all"] - base + t["aggregate_group"], 2)
     return out
+
+
+def layer_count(c, ab):
+    """Layer copies per timed step: enough draft bytes to exceed the 256 MB MALL
+    three times over, at most 64 layers and 40 GB of KV."""
+    layer_kv = int((c.prefix_len.astype(np.int64) + c.rows).sum()) * c.num_kv_heads * c.head_dim * 2 * (
+        2 if c.dtype == "bf16" else 4)
+    L = max(2, int(np.ceil(3 * 256e6 / max(sum(ab["draft"]) / max(c.gamma, 1), 1))))
+    return min(L, 64, max(2, int(40e9 // layer_kv))), layer_kv
+
+
+def sweep(args):
+    """Kernel cost of one layer iteration over a grid of gamma x selection ratio
+    (the cost half of the pages' tuning procedure: accepted-token rates need a
+    model and are not measured).  Per point: the whole iteration (verify with
+    export, aggregate, top-k, gamma draft steps) and its draft part, each over
+    all layer copies in one HIP graph, HIP events."""
+    import dataclasses
+    import torch
+    from verification_guided_sparse_amd import synth
+    from verification_guided_sparse_amd.runner import DeviceCase
+    gammas = [int(x) for x in args.sweep_gammas.split(",")]
+    pcts = [int(x) for x in args.sweep_k_pcts.split(",")]
+    base_cfg = synth.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    points = []
+    for gamma in gammas:
+        case = synth.make_case(dataclasses.replace(base_cfg, gamma=gamma))
+        for pct in pcts:
+            c = synth.with_k_pct(case, pct)
+            L, _ = layer_count(c, algorithmic_bytes(c, args.export))
+            layers = [DeviceCase(c, device=dev)]
+            layers += [DeviceCase(c, device=dev, like=layers[0]) for _ in range(L - 1)]
+            for lc in layers:
+                lc.iteration(export=args.export)
+            torch.cuda.synchronize()
+
+            def it():
+                for lc in layers:
+                    lc.verify(export=args.export)
+                    lc.aggregate(src=args.export, fuse_prepass=True)
+                    lc.topk(prepass_done=True)
+                for s in range(c.gamma):
+                    for lc in layers:
+                        lc.sparse(step=s)
+
+            def drafts():
+                for s in range(c.gamma):
+                    for lc in layers:
+                        lc.sparse(step=s)
+
+            us_it = timed_graph_us(it, L, reps=max(args.steps // 5, 3))
+            us_dr = timed_graph_us(drafts, L, reps=max(args.steps // 5, 3))
+            p = {"gamma": gamma, "k_pct": pct, "k": [int(x) for x in c.k], "layers": L,
+                 "us_per_iter": round(us_it, 2), "us_verify_select": round(us_it - us_dr, 2),
+                 "us_drafts": round(us_dr, 2), "us_per_draft_step": round(us_dr / max(gamma, 1), 2)}
+            points.append(p)
+            print(f"[sweep] {json.dumps(p)}", file=sys.stderr, flush=True)
+            del layers
+            torch.cuda.empty_cache()
+    print(json.dumps({"sweep": args.workload, "export": args.export, "unit": "us per layer iteration",
+                      "points": points}), flush=True)
 
 
 def breakdown(layers, c, export):

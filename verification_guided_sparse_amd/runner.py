@@ -51,8 +51,9 @@ class DeviceCase:
             self.prefix_len = _dev(c.prefix_len, dev)
             self.k = _dev(c.k, dev)
         else:
-            for n in ("q", "q_draft", "k_cache", "v_cache", "page_table", "prefix_len", "k"):
+            for n in ("q", "q_draft", "k_cache", "v_cache", "page_table", "prefix_len"):
                 setattr(self, n, getattr(like, n).clone())
+            self.k = _dev(c.k, dev)  # the budget may differ (same inputs, another k)
         f32 = dict(dtype=torch.float32, device=dev)
         i32 = dict(dtype=torch.int32, device=dev)
         mp = self.max_prefix

@@ -295,6 +295,12 @@ def make_case(cfg: Config | str, seed: int | None = None) -> Case:
                 prefix_len=prefix, k=k, heavy=heavy)
 
 
+def with_k_pct(case: Case, k_pct: int) -> Case:
+    """The same inputs with another selection budget k_b = round-half-up(P_b * k_pct / 100)."""
+    k = np.array([pct_round_half_up(int(p), k_pct) for p in case.prefix_len], dtype=np.int32)
+    return dataclasses.replace(case, cfg=dataclasses.replace(case.cfg, k_pct=k_pct), k=k)
+
+
 def new_token_rows(case: Case, it: int) -> tuple[np.ndarray, np.ndarray]:
     """Seeded K/V rows of one iteration's gamma + 1 new tokens, [B][R][Hkv][D] in the
     case's storage dtype (same scale as the cache, no heavy-hitter terms)."""
