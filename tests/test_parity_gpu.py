@@ -161,6 +161,11 @@ SMALL = {
                                        gamma=7),
     # empty prefixes (P = 0): the new tokens only, nothing to export or select
     "empty_prefix": lambda: synth.small("c2_qwen3_32k", prefix=(0, 3000, 0, 40), gamma=4, k_pct=50),
+    # every verify row-tile count at both head sizes: D = 128 with 3 row tiles
+    # (36 rows), D = 64 with 2 and 4 row tiles (32 and 64 rows)
+    "rows36_d128": lambda: synth.small("c2_qwen3_32k", prefix=(2500, 613), gamma=8),
+    "rows32_d64": lambda: synth.small("c5_gptoss_64k", prefix=(2000, 1203), gamma=3),
+    "rows64_d64": lambda: synth.small("c5_gptoss_64k", prefix=(2000, 2077, 45), gamma=7),
     # k = P: every prefix position selected
     "k_all": lambda: synth.small("c5_gptoss_64k", prefix=(300, 77), k_pct=100),
 }

@@ -67,8 +67,13 @@ bool use_mfma(const vg_shape *s) {
 #endif
 
 // Tiles in flight per wave of the verify kernel: at D = 128 two (one when 3 or
-// 4 row tiles leave no registers for a second), at D = 64 one.
-constexpr int verify_pf(int D, int NT) { return D == 128 ? (NT <= 2 ? VG_VERIFY_PF : 1) : VG_VERIFY_PF64; }
+// 4 row tiles leave no registers for a second); at D = 64 one with two
+// workgroups per CU, and two when 4 row tiles make the merge area too large
+// for a second workgroup (one tile per wave in flight on one workgroup per
+// CU is too few bytes in flight to stream HBM).
+constexpr int verify_pf(int D, int NT) {
+  return D == 128 ? (NT <= 2 ? VG_VERIFY_PF : 1) : (NT <= 3 ? VG_VERIFY_PF64 : 2);
+}
 
 // Launch plan and workspace layout of one attention call.  Verify lists are
 // long and may be ragged: the workgroups share their tiles evenly (stream-K).
