@@ -166,6 +166,10 @@ SMALL = {
     "rows36_d128": lambda: synth.small("c2_qwen3_32k", prefix=(2500, 613), gamma=8),
     "rows32_d64": lambda: synth.small("c5_gptoss_64k", prefix=(2000, 1203), gamma=3),
     "rows64_d64": lambda: synth.small("c5_gptoss_64k", prefix=(2000, 2077, 45), gamma=7),
+    # equal prefix lengths: with unpadded rows (max_prefix = P) the verify
+    # combine keeps its speculative first loads
+    "uniform_b3": lambda: synth.small("c5_gptoss_64k", prefix=(2077,) * 3),
+    "uniform_b16": lambda: synth.small("c2_qwen3_32k", prefix=(700,) * 16, paging="permuted", ramp=0, spans=0),
     # k = P: every prefix position selected
     "k_all": lambda: synth.small("c5_gptoss_64k", prefix=(300, 77), k_pct=100),
 }
@@ -179,9 +183,12 @@ def test_small_parity(torch_cuda, name):
     _run_chain(c, dc, refs, "raw")
 
 
-@pytest.mark.parametrize("name", ["c4_small", "c5_small", "short_prefixes"])
+@pytest.mark.parametrize("name", ["c4_small", "c5_small", "short_prefixes", "c2_small", "c3_small",
+                                  "uniform_b3", "uniform_b16"])
 def test_small_parity_unpadded_rows(torch_cuda, name):
-    """Export / score rows exactly max_prefix floats long (unaligned strides)."""
+    """Export / score rows exactly max_prefix floats long (unaligned strides).
+    With equal prefix lengths this is also the verify combine's speculation on
+    equal lengths taken (c2_small, c3_small, uniform_*) rather than dropped."""
     c = synth.make_case(SMALL[name]())
     dc, refs = _run_steps(c, pad=1)
     _run_chain(c, dc, refs, "group")

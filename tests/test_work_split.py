@@ -120,3 +120,14 @@ def test_fixed_pieces(harness, lens, Hkv, split):
         seg, sp = divmod(w, splits)
         assert (b, g, part) == (seg // Hkv, seg % Hkv, w)
         assert (e0, e1) == (min(lens[b], sp * split), min(lens[b], (sp + 1) * split))
+
+
+@pytest.mark.parametrize("L,B,Hkv,tile,W", [(131079, 1, 8, 32, 256), (65542, 4, 8, 32, 256),
+                                            (3001, 3, 8, 32, 40), (700, 16, 8, 32, 256),
+                                            (5, 2, 4, 32, 1000), (64, 7, 2, 64, 9)])
+def test_uniform_prefix_walk_matches_the_array_walk(harness, L, B, Hkv, tile, W):
+    """With every list of the same length, the closed-form tile prefix (the
+    kernels' speculation on equal lengths) gives exactly the pieces and
+    combine lookups of the array prefix."""
+    lens = [L] * B
+    assert run(harness, 2, lens, Hkv, tile, W) == run(harness, 0, lens, Hkv, tile, W)

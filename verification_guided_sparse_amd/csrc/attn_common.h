@@ -80,12 +80,19 @@ __device__ __forceinline__ void merge_o(MergeSmem<ROWS, D> &sm, float *part_o, i
 // ---- work split index math (host and device; the host build is tested) ----
 
 // Stream-K walk of workgroup w: tiles [t, t_end) remain, the next one in
-// sequence b.  pre[b] = tiles of sequences before b (pre[batch] = all).
+// sequence b.  pre[b] = tiles of sequences before b (pre[batch] = all): an
+// array, or UniformPre when every list has the same number of tiles.
 struct ShareWalk {
   int t, t_end, b;
 };
 
-__host__ __device__ inline ShareWalk share_walk_begin(const int *pre, int batch, int Hkv, int w, int W) {
+struct UniformPre {
+  int n;  // tiles of every list
+  __host__ __device__ int operator[](int b) const { return b * n; }
+};
+
+template <typename Pre>
+__host__ __device__ inline ShareWalk share_walk_begin(const Pre &pre, int batch, int Hkv, int w, int W) {
   ShareWalk s;
   const long long T = (long long)Hkv * pre[batch];
   s.t = (int)share_begin(w, T, W);
@@ -107,8 +114,8 @@ struct Piece {
 };
 
 // Next piece of a stream-K walk (call while s.t < s.t_end); len[b] = list lengths.
-template <typename LenFn>
-__host__ __device__ inline Piece share_walk_next(ShareWalk &s, const int *pre, int Hkv, int tile, int w,
+template <typename Pre, typename LenFn>
+__host__ __device__ inline Piece share_walk_next(ShareWalk &s, const Pre &pre, int Hkv, int tile, int w,
                                                  LenFn len) {
   int n = pre[s.b + 1] - pre[s.b];
   while (n == 0) {  // lists without tiles (none for valid inputs)
@@ -147,14 +154,15 @@ __host__ __device__ inline Piece fixed_piece(int w, int splits, int split_tokens
 // Partials of segment (b, g) for the combine: indices first + j, j < count.
 // With shared tiles, index first + j is only valid if workgroup w = first + j -
 // seg has a share that meets the segment (share_meets).
-__host__ __device__ inline void combine_range(const int *pre, int batch, int Hkv, int W, int b, int g,
+template <typename Pre>
+__host__ __device__ inline void combine_range(const Pre &pre, int batch, int Hkv, int W, int b, int g,
                                               int &first, int &count) {
   const long long T = (long long)Hkv * pre[batch];
   const int n = pre[b + 1] - pre[b];
   const long long S = (long long)Hkv * pre[b] + (long long)g * n;  // segment's first tile
   // workgroups whose share [share_begin(w), share_begin(w + 1)) meets [S, S + n)
-  int w_first = (int)(((S + 1) * W + T - 1) / T) - 1;
-  int w_last = (int)(((S + n) * W + T - 1) / T) - 1;
+  int w_first = (int)floor_div((S + 1) * W + T - 1, T) - 1;
+  int w_last = (int)floor_div((S + n) * W + T - 1, T) - 1;
   w_first = w_first < 0 ? 0 : (w_first > W - 1 ? W - 1 : w_first);
   w_last = w_last > W - 1 ? W - 1 : w_last;
   if (w_last < w_first) w_last = w_first;
@@ -162,7 +170,8 @@ __host__ __device__ inline void combine_range(const int *pre, int batch, int Hkv
   count = w_last - w_first + 1;
 }
 
-__host__ __device__ inline bool share_meets(const int *pre, int batch, int Hkv, int W, int w, int b, int g) {
+template <typename Pre>
+__host__ __device__ inline bool share_meets(const Pre &pre, int batch, int Hkv, int W, int w, int b, int g) {
   const long long T = (long long)Hkv * pre[batch];
   const int n = pre[b + 1] - pre[b];
   const long long S = (long long)Hkv * pre[b] + (long long)g * n;
@@ -191,36 +200,15 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
   const int row = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int Hkv = a.num_kv_heads, W = a.workgroups;
   const bool fixed = a.split_tokens > 0;
-  int first, np;
-  if (fixed) {  // partials seg * splits .. + splits - 1, all written
-    first = (b * Hkv + g) * a.splits;
-    np = a.splits;
-  } else {
-    load_tile_prefix(a, pre, sm4);
-    combine_range(pre, a.batch, Hkv, W, b, g, first, np);
-  }
-  const int seg = b * Hkv + g, M = a.rows, G = a.group_size;
+  const int seg = b * Hkv + g, M = a.rows;
   const int col = t % C, sg = t / C;
-  const size_t p0 = (size_t)first * M + row;  // partial j lives at p0 + j * M
-  const float *pml = a.part_ml + p0 * 2;
-  const float *po = a.part_o + p0 * D + 4 * col;
   const size_t ml_stride = (size_t)M * 2, o_stride = (size_t)M * D;
-
   float mt = kMInit, dt = 0.f;
   f32x4 at = {0.f, 0.f, 0.f, 0.f};
-  for (int j0 = sg; j0 < np; j0 += kBatch * SP) {
-    float m[kBatch], l[kBatch];
-    f32x4 o[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int j = j0 + i * SP;
-      bool ok = j < np;
-      // the workgroup's share may miss the segment (more workgroups than tiles)
-      if (ok && !fixed) ok = share_meets(pre, a.batch, Hkv, W, first + j - seg, b, g);
-      m[i] = ok ? pml[j * ml_stride] : kMInit;
-      l[i] = ok ? pml[j * ml_stride + 1] : 0.f;
-      o[i] = ok ? *reinterpret_cast<const f32x4 *>(po + j * o_stride) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+  float m[kBatch], l[kBatch];
+  f32x4 o[kBatch];
+  // Merges a batch into the running (max, denominator, sum).
+  auto accumulate = [&]() {
     float mb = mt;
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) mb = fmaxf(mb, m[i]);
@@ -234,7 +222,87 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
       at += w * o[i];
     }
     mt = mb;
+  };
+  // Batch j0, j0 + SP, ... of the partials of range [first, first + np)
+  // (partial j at (first + j) * M + row); those failing ok(partial index)
+  // count as empty.
+  auto load_batch = [&](int first, int np, int j0, auto ok_fn) {
+    const size_t p0 = (size_t)first * M + row;
+    const float *pml = a.part_ml + p0 * 2;
+    const float *po = a.part_o + p0 * D + 4 * col;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int j = j0 + i * SP;
+      const bool ok = j < np && ok_fn(first + j);
+      m[i] = ok ? pml[j * ml_stride] : kMInit;
+      l[i] = ok ? pml[j * ml_stride + 1] : 0.f;
+      o[i] = ok ? *reinterpret_cast<const f32x4 *>(po + j * o_stride) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto all = [](int) { return true; };
+
+  if (fixed) {  // partials seg * splits .. + splits - 1, all written
+    const int first = seg * a.splits, np = a.splits;
+    for (int j0 = sg; j0 < np; j0 += kBatch * SP) {
+      load_batch(first, np, j0, all);
+      accumulate();
+    }
+  } else {
+    // Shared tiles (verify lists).  Partial p of a segment's range is written
+    // if workgroup p - seg has a share that meets the segment, which holds for
+    // the whole range when every workgroup has tiles (W <= T).
+    //
+    // Speculation: with every list at its longest length (all prefixes equal
+    // to max_prefix) the range is known before the lengths are read, so its
+    // first batch is loaded together with them (issued unconditionally, a
+    // partial outside the range reading partial 0 of the range instead, and
+    // masked after) and kept if the lengths agree.
+    const int spec_len = a.max_prefix + a.nrows;
+    const UniformPre up{(spec_len + a.tile - 1) / a.tile};
+    const int p0 = first_prefix_len(a);  // in flight with the speculative loads
+    int first, np;
+    combine_range(up, a.batch, Hkv, W, b, g, first, np);
+    const bool up_all = W <= (long long)Hkv * up[a.batch];
+    {
+      const size_t q0 = (size_t)first * M + row;
+      const float *pml = a.part_ml + q0 * 2;
+      const float *po = a.part_o + q0 * D + 4 * col;
+      bool ok[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int j = sg + i * SP;
+        ok[i] = j < np && (up_all || share_meets(up, a.batch, Hkv, W, first + j - seg, b, g));
+        const int jj = ok[i] ? j : 0;
+        const f32x2 ml = *reinterpret_cast<const f32x2 *>(pml + jj * ml_stride);
+        m[i] = ml[0];
+        l[i] = ml[1];
+        o[i] = *reinterpret_cast<const f32x4 *>(po + jj * o_stride);
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (!ok[i]) {
+          m[i] = kMInit;
+          l[i] = 0.f;
+          o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+    const bool spec = load_tile_prefix(a, pre, sm4, nullptr, spec_len, true, p0);
+    if (!spec) combine_range(pre, a.batch, Hkv, W, b, g, first, np);
+    const bool every = W <= (long long)Hkv * pre[a.batch];
+    auto meets = [&](int p) { return share_meets(pre, a.batch, Hkv, W, p - seg, b, g); };
+    for (int j0 = sg; j0 < np; j0 += kBatch * SP) {
+      if (j0 != sg || !spec) {
+        if (every)
+          load_batch(first, np, j0, all);
+        else
+          load_batch(first, np, j0, meets);
+      }
+      accumulate();
+    }
   }
+  const int G = a.group_size;
+
   // merge the groups: max, then rescaled sums
   sm_m[t] = mt;
   __syncthreads();
@@ -257,17 +325,15 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
   }
 }
 
+// x of the first active lane (a wave-uniform value the compiler may keep in a
+// scalar register).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // Calls fn(b, g, part, e_begin, e_end) for each piece of this workgroup's work
 // (uniform across the block): entries [e_begin, e_end) of the list of segment
 // (b, g), whose partial result goes to index `part`.  With fixed splits a
 // workgroup past its list's end gets one empty piece (e_begin == e_end).
-// pre / sm4: LDS for load_tile_prefix.
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// Calls fn(b, g, part, e_begin, e_end) for each piece of this workgroup's work
-// (uniform across the block).  With fixed splits a workgroup past its list's
-// end gets one empty piece (e_begin == e_end).  pre / lens / sm4: LDS for
-// load_tile_prefix.
+// pre / lens / sm4: LDS for load_tile_prefix.
 template <typename Fn>
 __device__ __forceinline__ void for_each_piece(const AttnArgs &a, int *pre, int *lens, int *sm4, Fn fn) {
   const int W = a.workgroups, w = blockIdx.x, Hkv = a.num_kv_heads;

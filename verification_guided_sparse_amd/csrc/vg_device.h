@@ -203,26 +203,51 @@ __device__ __forceinline__ int32_t entry_slot(const AttnArgs &a, int b, const Se
 //    depends on the lengths, which suits short, latency-bound lists.
 constexpr int kMaxBatch = 1024;
 
+// Verify: the prefix length of sequence min(threadIdx.x, B - 1), loaded
+// ahead of load_tile_prefix so that other loads can be in flight with it
+// (unconditional and in bounds; the row count is added at use, so that
+// nothing waits for the load here).
+__device__ __forceinline__ int first_prefix_len(const AttnArgs &a) {
+  return a.prefix_len[min((int)threadIdx.x, a.batch - 1)];
+}
+
 // pre[b] = sum over b' < b of ceil(len_b' / tile), for b <= B, and, if `lens`
-// is given, lens[b] = len_b (LDS, all threads).
-__device__ __forceinline__ void load_tile_prefix(const AttnArgs &a, int *pre, int *sm4, int *lens = nullptr) {
-  int run = 0;
+// is given, lens[b] = len_b (LDS, all threads).  Returns (to all threads)
+// whether every list has length `uniform_len`.  Verify callers may pass
+// first_prefix_len(a) as p0 (have_p0) for sequences 0..255.
+__device__ __forceinline__ bool load_tile_prefix(const AttnArgs &a, int *pre, int *sm4, int *lens = nullptr,
+                                                 int uniform_len = -1, bool have_p0 = false, int p0 = 0) {
+  int run = 0, differs = 0;
   for (int b0 = 0; b0 < a.batch; b0 += 256) {
     const int b = b0 + (int)threadIdx.x;
-    const int len = b < a.batch ? seq_list(a, b).len : 0;
+    int len = 0;
+    if (b < a.batch) len = (b0 == 0 && have_p0) ? p0 + a.nrows : seq_list(a, b).len;
     const int n = (len + a.tile - 1) / a.tile;
     if (lens && b < a.batch) lens[b] = len;
+    differs |= (b < a.batch && len != uniform_len);
     int tot;
     const int ex = block_exclusive_scan(n, sm4, tot);
     if (b < a.batch) pre[b] = run + ex;
     run += tot;
   }
   if (threadIdx.x == 0) pre[a.batch] = run;
-  __syncthreads();
+  return !__syncthreads_or(differs);
+}
+
+// floor(num / den) for 0 <= num < 2^52 and 0 < den < 2^31: the double
+// quotient is within one of it and is corrected by one step (a 64-bit integer
+// division is a long software sequence on the GPU).
+__host__ __device__ inline long long floor_div(long long num, long long den) {
+  long long q = (long long)((double)num / (double)den);
+  if (q * den > num)
+    --q;
+  else if ((q + 1) * den <= num)
+    ++q;
+  return q;
 }
 
 __host__ __device__ inline long long share_begin(int w, long long T, int W) {
-  return (long long)w * T / W;
+  return floor_div((long long)w * T, W);
 }
 
 }  // namespace vg
