@@ -267,6 +267,51 @@ def test_topk_ties_and_edges(torch_cuda):
             assert np.array_equal(hs[b, :n], sr[b, :n]), (rep, b)
 
 
+def test_topk_max_prefix(torch_cuda):
+    """The longest score row the select kernels take (2^21 positions, 1024
+    chunks), with so many ties at the threshold that the candidates overflow
+    the LDS cache of the last pass; bit-exact, twice (the workspace comes back
+    clean)."""
+    import torch
+    from verification_guided_sparse_amd import _binding as vg
+    mp = 1 << 21
+    _say(f"[parity] top-k at max_prefix={mp}")
+    rng = np.random.default_rng(21)
+    s = rng.integers(-3, 4, size=(1, mp)).astype(np.float32)
+    P = np.array([mp], np.int32)
+    k = np.array([mp // 2 + 12345], np.int32)
+    max_k = int(k[0])
+    npg = mp // 16
+    pt = rng.permutation(npg).astype(np.int32)[None]
+    dev = dict(device="cuda")
+    ts = torch.from_numpy(s).cuda()
+    tP, tk, tpt = (torch.from_numpy(x).cuda() for x in (P, k, pt))
+    pos = torch.full((1, max_k), -1, dtype=torch.int32, **dev)
+    slot = torch.full((1, max_k), -1, dtype=torch.int32, **dev)
+    cnt = torch.zeros(1, dtype=torch.int32, **dev)
+    nbytes = vg.vg_topk_workspace_size(1, mp)
+    ws = torch.empty(nbytes, dtype=torch.uint8, **dev)
+    vg.vg_workspace_zero(ws, nbytes)
+    pr, sr, cr = oracle.topk(s.astype(np.float64), P, k, page_table=pt, max_k=max_k)
+    for rep in range(2):
+        vg.vg_topk_select(1, ts, mp, tP, tk, max_k, tpt, 16, npg, pos, slot, cnt, 0, ws, nbytes)
+        torch.cuda.synchronize()
+        assert np.array_equal(cnt.cpu().numpy(), cr)
+        assert np.array_equal(pos.cpu().numpy()[0], pr[0]), rep
+        assert np.array_equal(slot.cpu().numpy()[0], sr[0]), rep
+
+
+def test_max_batch_parity(torch_cuda):
+    """The largest batch the attention calls take (1024 sequences: four rounds
+    of the length scan, 2048 (sequence, KV head) lists), ragged short prefixes
+    including empty ones; every step against the oracle."""
+    pre = tuple(int(x) for x in np.random.default_rng(5).integers(0, 300, 1024))
+    c = synth.make_case(synth.small("c2_qwen3_32k", prefix=pre, num_q_heads=8, num_kv_heads=2, gamma=3,
+                                    ramp=0, spans=0, k_pct=20, paging="permuted"))
+    dc, refs = _run_steps(c)
+    _run_chain(c, dc, refs, "group")
+
+
 # ------------------------------------------------------------------ full sizes
 
 @pytest.mark.parametrize("name", ["c1_tiny", "c2_qwen3_32k", "c3_qwen3_128k", "c5_gptoss_64k", "c4_ragged_b8"])
