@@ -98,13 +98,24 @@ AttnPlan plan_attention(const vg_shape *s, int nrows, long long max_len, bool sp
   p.ok = s->batch <= kMaxBatch && bg * ((L + p.tile - 1) / p.tile) < (1LL << 31);
   if (sparse) {
     // Sparse draft lists are short and the call is latency-bound: fixed splits
-    // of 4 tiles (one per wave) while the workgroups fit one wave of residency
-    // (2 per CU), else of 8 tiles.  Fixed splits need no length lookup before
-    // the first load; workgroups past a list's end exit after writing an empty
-    // partial, and the hardware dispatcher balances ragged batches.
-    const long long unit = (long long)kWaves * p.tile;
-    const bool small = bg * ((L + unit - 1) / unit) <= 2LL * kCUs;
-    p.split_tokens = (int)(small ? unit : 2 * unit);
+    // of 4 tiles (one per wave) while all workgroups fit the kernel's
+    // residency, else of 8 tiles.  Where that leaves some CUs with two
+    // workgroups and others with one, the splits shrink to the smallest size
+    // that still keeps every workgroup resident: the busiest CU then has
+    // fewer tiles (C3: splits of 3 tiles on 440 workgroups instead of 4 on
+    // 336, 11.4 against 11.8 us per draft step).  Fixed splits need no length
+    // lookup before the first load; workgroups past a list's end exit after
+    // writing an empty partial, and the hardware dispatcher balances ragged
+    // batches.
+    const long long res = (long long)(p.mfma ? attn_occupancy(s->head_dim, p.nt, VG_SPARSE_PF, true) : 1) * kCUs;
+    const long long tiles = (L + p.tile - 1) / p.tile;  // of the longest list
+    long long split = bg * ((tiles + kWaves - 1) / kWaves) <= res ? kWaves : 2 * kWaves;  // in tiles
+    const long long wgs = bg * ((tiles + split - 1) / split);
+    if (wgs > kCUs && wgs <= res) {
+      const long long per_list = std::max(1LL, res / bg);
+      split = std::min(split, (tiles + per_list - 1) / per_list);
+    }
+    p.split_tokens = (int)(split * p.tile);
     p.splits = (int)((L + p.split_tokens - 1) / p.split_tokens);
     p.workgroups = (int)(bg * p.splits);
     n_part = p.workgroups;
