@@ -267,6 +267,46 @@ def test_topk_ties_and_edges(torch_cuda):
             assert np.array_equal(hs[b, :n], sr[b, :n]), (rep, b)
 
 
+def test_topk_moderate_ties(torch_cuda):
+    """Scores on a 1/64 grid: tens to hundreds of positions share the k-th
+    score (the last pass's short path through the threshold's tie group, as
+    opposed to the long path the integer-score cases take); bit-exact."""
+    import torch
+    from verification_guided_sparse_amd import _binding as vg
+    B, mp = 3, 300_000
+    rng = np.random.default_rng(64)
+    s = (np.round(rng.standard_normal((B, mp)) * 64) / 64).astype(np.float32)
+    P = np.array([300_000, 123_457, 40_001], np.int32)
+    k = np.array([15_000, 77_777, 2_001], np.int32)
+    max_k = int(k.max())
+    npg = -(-mp // 16)
+    pt = np.stack([rng.permutation(npg) for _ in range(B)]).astype(np.int32)
+    s64 = s.astype(np.float64)
+    for b in range(B):  # the threshold value is shared by many positions
+        kth = np.sort(s64[b, :P[b]])[::-1][k[b] - 1]
+        assert 10 < int((s64[b, :P[b]] == kth).sum()) < 1024
+    _say("[parity] top-k with moderate ties")
+    dev = dict(device="cuda")
+    ts = torch.from_numpy(s).cuda()
+    tP, tk, tpt = (torch.from_numpy(x).cuda() for x in (P, k, pt))
+    pos = torch.full((B, max_k), -1, dtype=torch.int32, **dev)
+    slot = torch.full((B, max_k), -1, dtype=torch.int32, **dev)
+    cnt = torch.zeros(B, dtype=torch.int32, **dev)
+    nbytes = vg.vg_topk_workspace_size(B, mp)
+    ws = torch.empty(nbytes, dtype=torch.uint8, **dev)
+    vg.vg_workspace_zero(ws, nbytes)
+    pr, sr, cr = oracle.topk(s64, P, k, page_table=pt, max_k=max_k)
+    for rep in range(2):
+        vg.vg_topk_select(B, ts, mp, tP, tk, max_k, tpt, 16, npg, pos, slot, cnt, 0, ws, nbytes)
+        torch.cuda.synchronize()
+        assert np.array_equal(cnt.cpu().numpy(), cr)
+        hp, hs = pos.cpu().numpy(), slot.cpu().numpy()
+        for b in range(B):
+            n = int(cr[b])
+            assert np.array_equal(hp[b, :n], pr[b, :n]), (rep, b)
+            assert np.array_equal(hs[b, :n], sr[b, :n]), (rep, b)
+
+
 def test_topk_max_prefix(torch_cuda):
     """The longest score row the select kernels take (2^21 positions, 1024
     chunks), with so many ties at the threshold that the candidates overflow

@@ -41,6 +41,7 @@ constexpr int kBins1 = 4096;                   // key bits [20, 32)
 constexpr int kBins23 = 1024;                  // key bits [10, 20), then [0, 10)
 constexpr int kMaxChunks = 1024;               // max_prefix <= 2^21
 constexpr int kCandCache = 12288;              // candidates a pass-3 workgroup keeps in LDS
+constexpr int kTieList = 1024;                 // pass 3 fast path: candidates sharing K*'s 22-bit prefix
 
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -86,7 +87,7 @@ struct SelArgs {
 // results are still being read.
 template <int PER>
 __device__ __forceinline__ int find_bin_regs(const uint32_t (&h)[PER], int nbins, int k, int *sm4,
-                                             int *res, int &above) {
+                                             int *res, int &above, int *count = nullptr) {
   const int t = threadIdx.x;
   const int top = nbins - PER * t;
   int local = 0;
@@ -95,6 +96,7 @@ __device__ __forceinline__ int find_bin_regs(const uint32_t (&h)[PER], int nbins
   if (t == 0) {
     res[0] = 0;
     res[1] = 0;
+    if (count) res[2] = 0;
   }
   int total;
   const int pre = block_exclusive_scan(local, sm4, total);  // its barriers order the reset above
@@ -107,6 +109,7 @@ __device__ __forceinline__ int find_bin_regs(const uint32_t (&h)[PER], int nbins
       if (!done && k <= run + c) {
         res[0] = top - 1 - i;
         res[1] = run;
+        if (count) res[2] = c;
         done = true;
       }
       run += c;
@@ -114,6 +117,7 @@ __device__ __forceinline__ int find_bin_regs(const uint32_t (&h)[PER], int nbins
   }
   __syncthreads();
   above = res[1];
+  if (count) *count = res[2];
   return res[0];
 }
 
@@ -289,6 +293,8 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
   __shared__ int cgt[kMaxChunks];       // per chunk: candidates above K*
   __shared__ int ceq[kMaxChunks];       // per chunk: candidates equal to K*
   __shared__ u32x2 cache[kCandCache];
+  __shared__ uint32_t tie[kTieList];   // fast path: candidates sharing K*'s 22-bit prefix
+  __shared__ int tie_n;
   __shared__ int sm4[4];
   __shared__ int sm_res[8];
   const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
@@ -362,12 +368,14 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
   }
   const int k1 = k_eff - above1;  // >= 1: rank of K* inside bin b1
   int above2;
-  const uint32_t b2 = (uint32_t)find_bin_regs<4>(h2, kBins23, k1, sm4, sm_res, above2);  // csum visible after
+  int n_b2;  // candidates sharing K*'s 22-bit prefix
+  if (t == 0) tie_n = 0;  // ordered before its atomics by find_bin_regs' barriers
+  const uint32_t b2 =
+      (uint32_t)find_bin_regs<4>(h2, kBins23, k1, sm4, sm_res, above2, &n_b2);  // csum visible after
   const int k2 = k1 - above2;
   const uint32_t pre22 = (b1 << 10) | b2;
   const int n_c = csum[nch];
   const u32x2 *cand = a.ws.cand + (size_t)b * a.max_prefix;
-  const bool cached = n_c <= kCandCache;
   // Candidates of chunk c are read by a fixed group of tpc consecutive threads
   // (tpc = 256 / nch rounded down to a power of two, at most a wave; for
   // nch > 256 every thread takes chunks t, t + 256, ...): no search for a
@@ -375,6 +383,56 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
   int tpc = 1;
   while (tpc < kWave && tpc * 2 * nch <= kSelThreads) tpc *= 2;
   const int sub = t % tpc, c_first = t / tpc, c_step = kSelThreads / tpc;
+  uint32_t kstar;
+  int ties;  // entries equal to K* to keep, lowest positions first
+  if (n_b2 <= kTieList) {
+    // Fast path: one pass over the candidates (keys only, from global) counts
+    // per chunk those above K*'s 22-bit prefix, and gathers the few sharing
+    // it (their low 10 bits and chunk) into LDS with their bit histogram.
+    // K* then follows from that histogram, and the gathered candidates
+    // complete the per-chunk counts above and equal to K*.
+    const uint32_t *ckey = reinterpret_cast<const uint32_t *>(cand);
+    for (int c = c_first; c < nch; c += c_step) {
+      const int n = csum[c + 1] - csum[c];
+      int gt = 0;
+      for (int i0 = sub; i0 < n; i0 += 8 * tpc) {
+        uint32_t kq[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) kq[u] = i0 + u * tpc < n ? ckey[2 * ((size_t)c * kChunk + i0 + u * tpc)] : 0u;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (i0 + u * tpc < n) {
+            const uint32_t hi = kq[u] >> 10;
+            gt += hi > pre22;
+            if (hi == pre22) {
+              atomicAdd(&lh[kq[u] & 1023u], 1u);
+              const int q = atomicAdd(&tie_n, 1);  // < n_b2 <= kTieList
+              if (q < kTieList) tie[q] = (kq[u] & 1023u) | ((uint32_t)c << 10);
+            }
+          }
+        }
+      }
+      for (int o = 1; o < tpc; o <<= 1) gt += __shfl_xor(gt, o);
+      if (sub == 0) {
+        cgt[c] = gt;
+        ceq[c] = 0;
+      }
+    }
+    __syncthreads();
+    uint32_t h3[4];
+    load_bins_desc<4>(lh, kBins23, h3);
+    int above3;
+    const uint32_t b3 = (uint32_t)find_bin_regs<4>(h3, kBins23, k2, sm4, sm_res + 3, above3);
+    kstar = (pre22 << 10) | b3;
+    ties = k2 - above3;
+    for (int i = t; i < min(n_b2, kTieList); i += kSelThreads) {
+      const uint32_t low = tie[i] & 1023u, c = tie[i] >> 10;
+      if (low > b3) atomicAdd(&cgt[c], 1);
+      else if (low == b3) atomicAdd(&ceq[c], 1);
+    }
+    __syncthreads();
+  } else {
+  const bool cached = n_c <= kCandCache;
   if (cached) {
     for (int c = c_first; c < nch; c += c_step) {
       const int n = csum[c + 1] - csum[c];
@@ -414,9 +472,9 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
   uint32_t h3[4];
   load_bins_desc<4>(lh, kBins23, h3);
   int above3;
-  const uint32_t b3 = (uint32_t)find_bin_regs<4>(h3, kBins23, k2, sm4, sm_res + 2, above3);
-  const uint32_t kstar = (pre22 << 10) | b3;
-  const int ties = k2 - above3;  // entries equal to K* to keep, lowest positions first
+  const uint32_t b3 = (uint32_t)find_bin_regs<4>(h3, kBins23, k2, sm4, sm_res + 3, above3);
+  kstar = (pre22 << 10) | b3;
+  ties = k2 - above3;
   // per chunk: candidates above and equal to K*, summed over the chunk's group
   for (int c = c_first; c < nch; c += c_step) {
     const int n = csum[c + 1] - csum[c];
@@ -442,6 +500,7 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
     }
   }
   __syncthreads();
+  }
   // Output offset of chunk w: entries above K* in earlier chunks plus the ties
   // they take, min(ties, equal keys in earlier chunks).
   int sel_before, eq_before;
@@ -463,15 +522,15 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int c = t * per + i;
       if (i < per && c == w) {
-        sm_res[4] = g_run + min(ties, e_run);
-        sm_res[5] = e_run;
+        sm_res[6] = g_run + min(ties, e_run);
+        sm_res[7] = e_run;
       }
       g_run += gv[i];
       e_run += ev[i];
     }
     __syncthreads();
-    sel_before = sm_res[4];
-    eq_before = sm_res[5];
+    sel_before = sm_res[6];
+    eq_before = sm_res[7];
   }
   // Select this chunk's entries in position order: one scan of the packed
   // (greater, equal) counts (each <= 2048) gives every thread's offset.
