@@ -170,6 +170,11 @@ SMALL = {
     # combine keeps its speculative first loads
     "uniform_b3": lambda: synth.small("c5_gptoss_64k", prefix=(2077,) * 3),
     "uniform_b16": lambda: synth.small("c2_qwen3_32k", prefix=(700,) * 16, paging="permuted", ramp=0, spans=0),
+    # keys rising along the sequence (a ramp over the whole prefix, no sink or
+    # heavy hitters): the running maximum keeps growing from tile to tile, so
+    # every rescale of the online softmax matters
+    "rising": lambda: synth.small("c2_qwen3_32k", prefix=(3000, 1500), ramp=3000, sink=False, hh_pct=0,
+                                  spans=0),
     # k = P: every prefix position selected
     "k_all": lambda: synth.small("c5_gptoss_64k", prefix=(300, 77), k_pct=100),
 }
@@ -195,7 +200,7 @@ def test_small_parity_unpadded_rows(torch_cuda, name):
     _run_chain(c, dc, refs, "raw")
 
 
-@pytest.mark.parametrize("name", ["c2_small", "c5_small", "short_prefixes"])
+@pytest.mark.parametrize("name", ["c2_small", "c5_small", "short_prefixes", "rising"])
 def test_small_parity_valu_bf16(torch_cuda, name):
     from verification_guided_sparse_amd import _binding as vg
     c = synth.make_case(SMALL[name]())
@@ -265,6 +270,34 @@ def test_topk_ties_and_edges(torch_cuda):
             n = int(cr[b])
             assert np.array_equal(hp[b, :n], pr[b, :n]), (rep, b)
             assert np.array_equal(hs[b, :n], sr[b, :n]), (rep, b)
+
+
+@pytest.mark.parametrize("name,kernel", [("c2_qwen3_32k", "auto"), ("c5_gptoss_64k", "auto"),
+                                         ("c2_qwen3_32k", "valu"), ("c1_tiny", "auto")])
+def test_single_key_gather_is_exact(torch_cuda, name, kernel):
+    """A row that sees exactly one key has softmax weight 1 on it, so its output
+    is that key's value row converted to fp32, bit for bit: verify row 0 over
+    an empty prefix, and a draft step over a one-entry tail with nothing
+    selected.  This checks the gathers through the page table and the
+    normalisation of both kernels exactly."""
+    import torch
+    from verification_guided_sparse_amd import _binding as vg
+    from verification_guided_sparse_amd.runner import DeviceCase
+    c = synth.make_case(synth.small(name, prefix=(0, 0, 0), gamma=3, paging="permuted"))
+    kern = {"auto": vg.VG_KERNEL_AUTO, "valu": vg.VG_KERNEL_VALU}[kernel]
+    _say(f"[parity] single-key gather {name} kernel={kernel}")
+    dc = DeviceCase(c, kernel=kern)
+    dc.verify(export="group")
+    dc.window(n_sink=0)  # k = 0 for an empty prefix: nothing selected
+    dc.sparse(step=0)    # tail_len 1: position 0 only
+    torch.cuda.synchronize()
+    G = c.num_q_heads // c.num_kv_heads
+    v = c.v_cache if c.dtype == "f32" else synth.bf16_bits_to_f32(c.v_cache)
+    slot0 = c.page_table[:, 0].astype(np.int64) * 16  # position 0 of each sequence
+    want = np.stack([np.repeat(v[slot0[b]], G, axis=0) for b in range(c.batch)])  # [B][Hq][D]
+    assert np.array_equal(dc.host("sel_count"), np.zeros(c.batch, np.int32))
+    assert np.array_equal(dc.host("out")[:, 0], want)
+    assert np.array_equal(dc.host("draft_out")[:, 0], want)
 
 
 def test_topk_moderate_ties(torch_cuda):

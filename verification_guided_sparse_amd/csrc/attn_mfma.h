@@ -251,7 +251,9 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
     }
   }
 
-  // Online softmax (base 2) and P^T fragments.  Masking is only needed on
+  // Online softmax (base 2) and P^T fragments.  The scaled logits are rounded
+  // once (no multiply-add contraction into the exponent's argument), so the
+  // entry that sets the running maximum gets p = 1 exactly.  Masking is only needed on
   // tiles that reach past the chunk's end or into the causal part of the key
   // list; O is rescaled only if some row's running maximum grew (otherwise
   // every alpha is exactly 1).
@@ -268,7 +270,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          x[tt][c] = st[tt][rt][c] * a.scale_log2;
+          x[tt][c] = __fmul_rn(st[tt][rt][c], a.scale_log2);
           mx = fmaxf(mx, x[tt][c]);
         }
     } else {
@@ -279,7 +281,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
         for (int c = 0; c < 4; ++c) {
           const int e = e0 + tt * 16 + 4 * q4 + c;
           const bool ok = (e < e_end) && (e < vis);
-          x[tt][c] = ok ? st[tt][rt][c] * a.scale_log2 : kNegInf;
+          x[tt][c] = ok ? __fmul_rn(st[tt][rt][c], a.scale_log2) : kNegInf;
           mx = fmaxf(mx, x[tt][c]);
         }
     }

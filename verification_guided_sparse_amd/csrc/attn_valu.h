@@ -158,15 +158,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_valu_kernel(AttnArgs a) {
       }
 
       // Softmax with the wave reductions on DPP / lane swaps (no LDS round
-      // trips); the running max and rescale factor are wave-uniform.
+      // trips); the running max and rescale factor are wave-uniform.  The
+      // scaled logit is rounded once (no multiply-add contraction into the
+      // exponent's argument), so the entry that sets the maximum gets p = 1.
       float alpha[MR];
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
         const int vis = s.vis0 + m / G;
         const bool ok = (e < e_end) && (e < vis);
-        const float x = ok ? acc[m] * a.scale_log2 : kNegInf;
-        const float m_new = __builtin_amdgcn_readfirstlane(fmaxf(m_run[m], wave_max_dpp(x)));
-        alpha[m] = __builtin_amdgcn_readfirstlane(exp2_fast(m_run[m] - m_new));
+        const float x = ok ? __fmul_rn(acc[m], a.scale_log2) : kNegInf;
+        const float m_new = first_lane(fmaxf(m_run[m], wave_max_dpp(x)));
+        alpha[m] = first_lane(exp2_fast(m_run[m] - m_new));
         m_run[m] = m_new;
         const float p = exp2_fast(x - m_new);
         l_run[m] = l_run[m] * alpha[m] + p;

@@ -27,6 +27,12 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
 // Exponential in base 2 (hardware v_exp_f32).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lane 0's value of a float, as a wave-uniform value.  (readfirstlane takes
+// an int: passing the float itself would convert its value, not its bits.)
+__device__ __forceinline__ float first_lane(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
 // Lane l exchanges with lane l ^ 32 / l ^ 16 through v_permlane32_swap /
 // v_permlane16_swap: swapping a register with itself leaves {lower, upper}
 // halves (resp. {even, odd} 16-lane rows) in the two results, so combining
