@@ -182,26 +182,32 @@ __host__ __device__ inline bool share_meets(const Pre &pre, int batch, int Hkv, 
 // Combining the partials of segment (b, g) for one output row:
 //   out = sum_w c_w O_w / sum_w c_w l_w,  c_w = exp2(m_w - max_w m_w)
 // over the workgroups w whose share of the tiles meets the segment (or over
-// the segment's fixed splits).  One
-// 256-thread block per row; thread (group sg, float4 column col) takes
+// the segment's fixed splits).  RPB rows per 256-thread block (fewer blocks
+// when each row has few partials: many tiny blocks are limited by how fast
+// they are dispatched); thread (group sg, float4 column col) of a row takes
 // partials sg, sg + SP, ... in batches whose (m, l, O) loads are all in
 // flight together, keeping an online (max, denominator, sum) state; the
 // groups' states are then merged through LDS.
-template <int D>
+template <int D, int RPB>
 __global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
-  constexpr int C = D / 4;          // float4 columns of a row
-  constexpr int SP = kThreads / C;  // partial groups
+  constexpr int C = D / 4;              // float4 columns of a row
+  constexpr int TPR = kThreads / RPB;   // threads per row
+  constexpr int SP = TPR / C;           // partial groups per row
+  static_assert(SP >= 1, "a row needs at least one partial group");
   constexpr int kBatch = 8;
   __shared__ int pre[kMaxBatch + 1];
   __shared__ int sm4[4];
   __shared__ float sm_m[kThreads];
-  __shared__ float sm_d[SP];
+  __shared__ float sm_d[RPB * SP];
   __shared__ f32x4 sm_o[kThreads];
-  const int row = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int rg = t / TPR, tr = t % TPR;  // this thread's row in the block, its index in the row
+  const int row = blockIdx.x * RPB + rg;
   const int Hkv = a.num_kv_heads, W = a.workgroups;
   const bool fixed = a.split_tokens > 0;
   const int seg = b * Hkv + g, M = a.rows;
-  const int col = t % C, sg = t / C;
+  const bool live = row < M;  // the last block may hold fewer rows (no early exit: barriers)
+  const int col = tr % C, sg = tr / C;
   const size_t ml_stride = (size_t)M * 2, o_stride = (size_t)M * D;
   float mt = kMInit, dt = 0.f;
   f32x4 at = {0.f, 0.f, 0.f, 0.f};
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int j = j0 + i * SP;
-      const bool ok = j < np && ok_fn(first + j);
+      const bool ok = live && j < np && ok_fn(first + j);
       m[i] = ok ? pml[j * ml_stride] : kMInit;
       l[i] = ok ? pml[j * ml_stride + 1] : 0.f;
       o[i] = ok ? *reinterpret_cast<const f32x4 *>(po + j * o_stride) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -264,14 +270,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
     combine_range(up, a.batch, Hkv, W, b, g, first, np);
     const bool up_all = W <= (long long)Hkv * up[a.batch];
     {
-      const size_t q0 = (size_t)first * M + row;
+      const size_t q0 = (size_t)first * M + (live ? row : 0);
       const float *pml = a.part_ml + q0 * 2;
       const float *po = a.part_o + q0 * D + 4 * col;
       bool ok[kBatch];
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
         const int j = sg + i * SP;
-        ok[i] = j < np && (up_all || share_meets(up, a.batch, Hkv, W, first + j - seg, b, g));
+        ok[i] = live && j < np && (up_all || share_meets(up, a.batch, Hkv, W, first + j - seg, b, g));
         const int jj = ok[i] ? j : 0;
         const f32x2 ml = *reinterpret_cast<const f32x2 *>(pml + jj * ml_stride);
         m[i] = ml[0];
@@ -303,24 +309,25 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
   }
   const int G = a.group_size;
 
-  // merge the groups: max, then rescaled sums
+  // merge each row's groups: max, then rescaled sums
+  const int rb = rg * TPR;  // this row's threads in the block
   sm_m[t] = mt;
   __syncthreads();
   float mx = kMInit;
-  for (int j = 0; j < SP; ++j) mx = fmaxf(mx, sm_m[j * C + col]);
+  for (int j = 0; j < SP; ++j) mx = fmaxf(mx, sm_m[rb + j * C + col]);
   const float r = exp2_fast(mt - mx);
   sm_o[t] = at * r;
-  if (col == 0) sm_d[sg] = dt * r;
+  if (col == 0) sm_d[rg * SP + sg] = dt * r;
   __syncthreads();
-  if (t < C) {
-    f32x4 acc = sm_o[t];
-    float den = sm_d[0];
+  if (live && tr < C) {
+    f32x4 acc = sm_o[rb + tr];
+    float den = sm_d[rg * SP];
     for (int j = 1; j < SP; ++j) {
-      acc += sm_o[j * C + t];
-      den += sm_d[j];
+      acc += sm_o[rb + j * C + tr];
+      den += sm_d[rg * SP + j];
     }
     const int qr = row / G, h = g * G + row % G;
-    *reinterpret_cast<f32x4 *>(a.out + (((size_t)b * a.nrows + qr) * a.num_q_heads + h) * D + 4 * t) =
+    *reinterpret_cast<f32x4 *>(a.out + (((size_t)b * a.nrows + qr) * a.num_q_heads + h) * D + 4 * tr) =
         acc * (1.0f / den);
   }
 }

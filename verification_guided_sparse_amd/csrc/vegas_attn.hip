@@ -167,8 +167,18 @@ void launch_valu_t(int mr, const AttnArgs &a, dim3 grid, hipStream_t st) {
   }
 }
 
-// Attention kernel over the shared key lists, then one combine block per
-// (row, KV head, sequence).
+template <int D>
+void launch_combine(int rpb, const AttnArgs &a, dim3 grid, hipStream_t st) {
+  switch (rpb) {
+    case 1: hipLaunchKernelGGL((combine_kernel<D, 1>), grid, dim3(kThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((combine_kernel<D, 2>), grid, dim3(kThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((combine_kernel<D, 4>), grid, dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((combine_kernel<D, 8>), grid, dim3(kThreads), 0, st, a); break;
+  }
+}
+
+// Attention kernel over the shared key lists, then combine blocks of one or
+// more rows per (KV head, sequence).
 vg_status launch_attention(const vg_shape *s, const AttnPlan &p, AttnArgs &a, char *ws,
                            hipStream_t st) {
   a.part_o = reinterpret_cast<float *>(ws + p.off_part_o);
@@ -190,11 +200,16 @@ vg_status launch_attention(const vg_shape *s, const AttnPlan &p, AttnArgs &a, ch
     if (s->head_dim == 128) launch_valu_t<float, 128>(p.mr, a, grid, st);
     else launch_valu_t<float, 64>(p.mr, a, grid, st);
   }
-  const dim3 cgrid(p.rows, s->num_kv_heads, s->batch);
-  if (s->head_dim == 128)
-    hipLaunchKernelGGL((combine_kernel<128>), cgrid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((combine_kernel<64>), cgrid, dim3(kThreads), 0, st, a);
+  // Rows per combine block: as many as leave each row enough partial groups
+  // to load its (at most) np partials in one batch of 8 per thread.
+  const int cols = s->head_dim / 4;
+  const long long bg = (long long)s->batch * s->num_kv_heads;
+  const long long np = p.split_tokens > 0 ? p.splits : (p.workgroups + bg - 1) / bg + 1;
+  int rpb = 1;
+  while (rpb < 8 && (kThreads / (2 * rpb)) / cols * 8 >= np && kThreads / (2 * rpb) >= cols) rpb *= 2;
+  const dim3 cgrid((p.rows + rpb - 1) / rpb, s->num_kv_heads, s->batch);
+  if (s->head_dim == 128) launch_combine<128>(rpb, a, cgrid, st);
+  else launch_combine<64>(rpb, a, cgrid, st);
   return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
 }
 
