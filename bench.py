@@ -130,8 +130,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs the path on a single MI355X; "
-              "run it with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the path runs on a single MI355X and has no "
+              "multi-GPU mode; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -56,7 +56,7 @@ extern "C" {
 typedef int32_t vg_status;
 #define VG_OK 0
 #define VG_ERR_INVALID_ARG 1  /* a null/misaligned pointer or an out-of-range argument */
-#define VG_ERR_UNSUPPORTED 2  /* a valid shape this build has no kernel for */
+#define VG_ERR_UNSUPPORTED 2  /* a valid shape the library has no kernel for */
 #define VG_ERR_WORKSPACE 3    /* workspace missing or smaller than the size query says */
 #define VG_ERR_HIP 4          /* the HIP runtime rejected a launch */
 

@@ -63,7 +63,8 @@ class Config:
     seed: int = 0
 
 
-# The five workloads.  Numbers follow the configurations the build is measured on.
+# The five workloads: a small f32 case, then the Qwen3-8B- and gpt-oss-20b-shaped attention
+# layers at 32K to 128K tokens of context.
 CONFIGS: dict[str, Config] = {
     "c1_tiny": Config(
         name="c1_tiny", batch=1, prefix=(2048,), num_q_heads=8, num_kv_heads=2,
