@@ -300,6 +300,64 @@ def test_single_key_gather_is_exact(torch_cuda, name, kernel):
     assert np.array_equal(dc.host("draft_out")[:, 0], want)
 
 
+@pytest.mark.parametrize("name,n_q,kernel", [("c2_small", 2, "auto"), ("c2_small", 5, "auto"),
+                                              ("c3_small", 7, "auto"), ("c5_small", 3, "auto"),
+                                              ("c5_small", 6, "auto"), ("c4_small", 4, "auto"),
+                                              ("short_prefixes", 3, "auto"), ("c2_small", 3, "valu"),
+                                              ("c1_tiny", 5, "auto")])
+def test_sparse_multi_row_draft(torch_cuda, name, n_q, kernel):
+    """Sparse attention for n_q > 1 query rows in one call: row j attends the
+    selected positions and the tail up to its own position (tail_len - n_q + j + 1
+    of the new tokens), so the rows share the selection and differ only in the
+    causal tail.  A seeded random selection of k_b positions per sequence stands
+    in for the top-k (the kernel sees only slots)."""
+    import torch
+    from verification_guided_sparse_amd import _binding as vg
+    from verification_guided_sparse_amd.runner import DeviceCase, _dev
+    c = synth.make_case(SMALL[name]())
+    R = c.rows
+    assert 1 <= n_q <= R
+    _say(f"[parity] sparse multi-row {name} n_q={n_q} kernel={kernel}")
+    kern = {"auto": vg.VG_KERNEL_AUTO, "valu": vg.VG_KERNEL_VALU}[kernel]
+    dc = DeviceCase(c, kernel=kern, max_tail=R)
+    rng = np.random.default_rng(4242 + n_q)
+    pos = np.full((c.batch, dc.max_k), -1, np.int32)
+    cnt = np.zeros(c.batch, np.int32)
+    for b in range(c.batch):
+        P = int(c.prefix_len[b])
+        kb = min(int(c.k[b]), P)
+        pos[b, :kb] = np.sort(rng.choice(P, size=kb, replace=False))
+        cnt[b] = kb
+    slot = np.full_like(pos, -1)
+    for b in range(c.batch):
+        p = pos[b, :cnt[b]].astype(np.int64)
+        slot[b, :cnt[b]] = c.page_table[b, p // c.page_size] * c.page_size + p % c.page_size
+    q = np.ascontiguousarray(c.q[:, R - n_q:])  # the last n_q verify rows as draft rows
+    tail_len = np.full(c.batch, R, np.int32)
+    dev = dc.device
+    out = torch.zeros(c.batch, n_q, c.num_q_heads, c.head_dim, dtype=torch.float32, device=dev)
+    ws_bytes = vg.vg_sparse_draft_workspace_size(dc.shape, n_q, dc.max_k, R)
+    ws = dc._workspace(ws_bytes)
+    vg.vg_sparse_draft_attention(dc.shape, _dev(q, dev), n_q, dc.k_cache, dc.v_cache,
+                                 _dev(slot, dev), _dev(cnt, dev), dc.max_k,
+                                 dc.page_table, dc.tail_start, _dev(tail_len, dev), R,
+                                 out, ws, ws_bytes)
+    torch.cuda.synchronize()
+    o_ref = oracle.sparse(q, c.k_cache, c.v_cache, c.page_table, pos, cnt, c.prefix_len, tail_len,
+                          c.scale, nthreads=NTHREADS)
+    _check(parity.output_gate(out.cpu().numpy(), o_ref), f"sparse multi-row n_q={n_q}")
+    # the last row sees every new token, as a one-row call over the whole tail does
+    out1 = torch.zeros(c.batch, 1, c.num_q_heads, c.head_dim, dtype=torch.float32, device=dev)
+    ws1_bytes = vg.vg_sparse_draft_workspace_size(dc.shape, 1, dc.max_k, R)
+    ws1 = dc._workspace(ws1_bytes)
+    vg.vg_sparse_draft_attention(dc.shape, _dev(q[:, -1:], dev), 1,
+                                 dc.k_cache, dc.v_cache, _dev(slot, dev),
+                                 _dev(cnt, dev), dc.max_k, dc.page_table, dc.tail_start,
+                                 _dev(tail_len, dev), R, out1, ws1, ws1_bytes)
+    torch.cuda.synchronize()
+    _check(parity.output_gate(out1.cpu().numpy(), o_ref[:, -1:]), "sparse one-row call, whole tail")
+
+
 def test_topk_moderate_ties(torch_cuda):
     """Scores on a 1/64 grid: tens to hundreds of positions share the k-th
     score (the last pass's short path through the threshold's tie group, as
