@@ -177,6 +177,10 @@ SMALL = {
                                   spans=0),
     # k = P: every prefix position selected
     "k_all": lambda: synth.small("c5_gptoss_64k", prefix=(300, 77), k_pct=100),
+    # fp32 cache at D = 128 (the VALU kernel's other head size), ragged, permuted pool
+    "f32_d128": lambda: synth.small("c4_ragged_b8", prefix=(1200, 333, 2049), dtype="f32"),
+    # fp32 with G = 8 query heads per KV head at D = 64
+    "f32_g8": lambda: synth.small("c5_gptoss_64k", prefix=(900, 1601), dtype="f32"),
 }
 
 
