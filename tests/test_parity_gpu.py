@@ -496,7 +496,7 @@ def test_graph_replay_matches_eager(torch_cuda):
             assert np.array_equal(got["sel_slot"][b, :k], ref["sel_slot"][b, :k]), (rep, b)
 
 
-@pytest.mark.parametrize("name", ["c2_small", "c5_small", "short_prefixes", "gamma0"])
+@pytest.mark.parametrize("name", ["c2_small", "c5_small", "short_prefixes", "gamma0", "c1_tiny"])
 def test_full_collection_parity(torch_cuda, name):
     """All-rows export (the objective over every verify row): logits of every row,
     group sums over every row, aggregation over gamma+1 rows, and the chain."""
@@ -578,7 +578,7 @@ def test_kv_append_bit_exact(torch_cuda, name):
            "group after append")
 
 
-@pytest.mark.parametrize("name", ["c4_small", "c5_small", "short_prefixes"])
+@pytest.mark.parametrize("name", ["c4_small", "c5_small", "short_prefixes", "c1_tiny"])
 def test_iterations_on_device(torch_cuda, name):
     """Several iterations with the cache, the prefix lengths and the selection kept on
     the device: append the new tokens, verify (group export), aggregate, top-k, the
