@@ -211,15 +211,24 @@ def test_small_parity_valu_bf16(torch_cuda, name):
     _run_steps(c, kernel=vg.VG_KERNEL_VALU)
 
 
-def test_page_permutation_bit_identical(torch_cuda):
+@pytest.mark.parametrize("base,kw,kernel", [
+    ("c2_qwen3_32k", dict(prefix=(2500, 1200)), "auto"),           # MFMA, D = 128
+    ("c5_gptoss_64k", dict(prefix=(2000, 3100)), "auto"),          # MFMA, D = 64, G = 8
+    ("c4_ragged_b8", dict(prefix=(900, 2100), dtype="f32"), "auto"),  # VALU, fp32
+    ("c2_qwen3_32k", dict(prefix=(2500, 1200)), "valu"),           # VALU, bf16
+])
+def test_page_permutation_bit_identical(torch_cuda, base, kw, kernel):
     """Same logical data under identity and permuted page tables: identical bits."""
     import torch
+    from verification_guided_sparse_amd import _binding as vg
     from verification_guided_sparse_amd.runner import DeviceCase
-    cfg = synth.small("c2_qwen3_32k", prefix=(2500, 1200))
+    cfg = synth.small(base, **kw)
+    kern = {"auto": vg.VG_KERNEL_AUTO, "valu": vg.VG_KERNEL_VALU}[kernel]
+    _say(f"[parity] page permutation {base} {kw} kernel={kernel}")
     res = []
     for paging in ("identity", "permuted"):
         c = synth.make_case(synth.dataclasses.replace(cfg, paging=paging))
-        dc = DeviceCase(c)
+        dc = DeviceCase(c, kernel=kern)
         dc.iteration(export="both")
         torch.cuda.synchronize()
         res.append((dc.host("out"), dc.host("logits"), dc.host("group"), dc.host("scores"),
