@@ -285,6 +285,61 @@ def test_topk_ties_and_edges(torch_cuda):
             assert np.array_equal(hs[b, :n], sr[b, :n]), (rep, b)
 
 
+def test_out_of_range_counts_are_clamped(torch_cuda):
+    """Device-side lengths the host cannot check are clamped to what the
+    buffers were sized for, never turned into out-of-bounds accesses: top-k
+    takes P_b in [0, max_prefix] and k_b in [0, min(P_b, max_k)]; the sparse
+    draft takes sel_count in [0, max_k] and tail_len in [1, max_tail]."""
+    import torch
+    from verification_guided_sparse_amd import _binding as vg
+    from verification_guided_sparse_amd.runner import DeviceCase, _dev
+    # top-k
+    B, mp, max_k = 4, 3000, 400
+    rng = np.random.default_rng(5)
+    s = rng.standard_normal((B, mp)).astype(np.float32)
+    P = np.array([3000, 5000, -5, 1000], np.int32)  # 5000 > max_prefix, -5 < 0
+    k = np.array([900, 200, 5, -3], np.int32)         # 900 > max_k, -3 < 0
+    pt = np.arange(B * 200, dtype=np.int32).reshape(B, 200)
+    ts, tP, tk, tpt = (torch.from_numpy(x).cuda() for x in (s, P, k, pt))
+    pos = torch.full((B, max_k), -1, dtype=torch.int32, device="cuda")
+    slot = torch.full((B, max_k), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(B, dtype=torch.int32, device="cuda")
+    nbytes = vg.vg_topk_workspace_size(B, mp)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    vg.vg_workspace_zero(ws, nbytes)
+    vg.vg_topk_select(B, ts, mp, tP, tk, max_k, tpt, 16, 200, pos, slot, cnt, 0, ws, nbytes)
+    torch.cuda.synchronize()
+    Pc = np.clip(P, 0, mp)
+    kc = np.minimum(np.clip(k, 0, None), np.minimum(Pc, max_k)).astype(np.int32)
+    pr, sr, cr = oracle.topk(s.astype(np.float64), Pc, kc, page_table=pt, max_k=max_k)
+    assert np.array_equal(cnt.cpu().numpy(), kc)
+    assert np.array_equal(cr, kc)
+    hp, hs = pos.cpu().numpy(), slot.cpu().numpy()
+    for b in range(B):
+        n = int(kc[b])
+        assert np.array_equal(hp[b, :n], pr[b, :n]), b
+        assert np.array_equal(hs[b, :n], sr[b, :n]), b
+        assert np.all(hp[b, n:] == -1), b  # nothing written past the count
+
+    # sparse draft: a full list of max_k valid slots, sel_count past max_k,
+    # tail_len past max_tail
+    c = synth.make_case(synth.small("c2_qwen3_32k", prefix=(3001, 1200)))
+    dc = DeviceCase(c)
+    mk = dc.max_k
+    sel = np.stack([np.sort(rng.choice(int(c.prefix_len[b]), size=mk, replace=False))
+                    for b in range(c.batch)]).astype(np.int32)
+    slots = (c.page_table[np.arange(c.batch)[:, None], sel // 16] * 16 + sel % 16).astype(np.int32)
+    over_cnt = np.full(c.batch, mk + 100, np.int32)
+    over_tail = np.full(c.batch, dc.max_tail + 3, np.int32)
+    dc.sparse(step=0, sel_slot=_dev(slots, dc.device), sel_count=_dev(over_cnt, dc.device),
+              tail_len=_dev(over_tail, dc.device))
+    torch.cuda.synchronize()
+    want = oracle.sparse(np.ascontiguousarray(c.q_draft[0][:, None]), c.k_cache, c.v_cache, c.page_table,
+                         sel, np.full(c.batch, mk, np.int32), c.prefix_len,
+                         np.full(c.batch, dc.max_tail, np.int32), c.scale, nthreads=NTHREADS)
+    _check(parity.output_gate(dc.host("draft_out"), want), "sparse draft with clamped counts")
+
+
 @pytest.mark.parametrize("name,kernel", [("c2_qwen3_32k", "auto"), ("c5_gptoss_64k", "auto"),
                                          ("c2_qwen3_32k", "valu"), ("c1_tiny", "auto")])
 def test_single_key_gather_is_exact(torch_cuda, name, kernel):

@@ -15,6 +15,23 @@ constexpr int kWaves = 4;           // waves per attention workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxRows = 64;        // rows (query rows x heads of a group) per workgroup
 
+// PF = tiles in flight per wave.  PF == 1: load, then compute, two waves per
+// SIMD; PF > 1: a ring of PF tiles, one wave per SIMD.
+// SPARSE selects the sparse draft (true) or verify (false) instantiation; the
+// local copy of the arguments carries it as a constant, so every helper that
+// tests a.sparse folds to one path.
+// Workgroups per CU the kernel is compiled for.  The sparse draft takes two
+// where its rows fit the registers of two (at D = 128 with 2 row tiles they
+// would spill).  Verify at D = 64 with at most
+// 3 row tiles fits two workgroups (one tile in flight per wave): the second
+// workgroup's waves hide the first's softmax work, which per byte is twice
+// that of D = 128.  D = 128 verify keeps one workgroup with two tiles in
+// flight (at two it spills and is slower).
+constexpr int attn_occupancy(int D, int NT, int PF, bool sparse) {
+  return sparse ? ((PF == 1 && (NT == 1 || (D == 64 && NT == 2))) ? 2 : 1)
+                : ((D == 64 && NT <= 3 && PF == 1) ? 2 : 1);
+}
+
 // LDS layout of the merge step.  O is staged as [wave][row][D] floats.
 template <int ROWS, int D>
 struct MergeSmem {

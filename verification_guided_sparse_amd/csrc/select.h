@@ -79,6 +79,15 @@ struct SelArgs {
   SelWs ws;
 };
 
+// Prefix length and selection size of sequence b, clamped to what the
+// buffers were sized for: 0 <= P <= max_prefix and 0 <= kk <= min(P, max_k).
+__device__ __forceinline__ int sel_prefix(const SelArgs &a, int b) {
+  return min(max(a.prefix_len[b], 0), a.max_prefix);
+}
+__device__ __forceinline__ int sel_k(const SelArgs &a, int b, int P) {
+  return min(min(max(a.k[b], 0), P), a.max_k);
+}
+
 // Rank search over a histogram held in registers: thread t holds the PER bins
 // [nbins - PER (t + 1), nbins - PER t) in descending order (h[0] = the
 // highest).  Finds the bin holding the k-th largest key (1 <= k <= total) and,
@@ -148,7 +157,7 @@ template <bool AGG, bool HIST>
 __global__ __launch_bounds__(kP1Threads) void select_pass1_kernel(SelArgs a) {
   __shared__ uint32_t lh[kBins1];
   const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
-  const int P = a.prefix_len[b];
+  const int P = sel_prefix(a, b);
   const int nch = (P + kChunk - 1) / kChunk;
   if (w >= nch) return;
   if (HIST) {
@@ -232,8 +241,8 @@ __global__ __launch_bounds__(kSelThreads) void select_pass2_kernel(SelArgs a) {
   __shared__ int sm4[4];
   __shared__ int sm_res[2];
   const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
-  const int P = a.prefix_len[b];
-  const int k_eff = min(a.k[b], P);
+  const int P = sel_prefix(a, b);
+  const int k_eff = sel_k(a, b, P);
   const int nch = (P + kChunk - 1) / kChunk;
   if (w >= nch) return;
   const int j0 = w * kChunk + t * kPerThread;
@@ -298,8 +307,8 @@ __global__ __launch_bounds__(kSelThreads) void select_pass3_kernel(SelArgs a) {
   __shared__ int sm4[4];
   __shared__ int sm_res[8];
   const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
-  const int P = a.prefix_len[b];
-  const int k_eff = min(a.k[b], P);
+  const int P = sel_prefix(a, b);
+  const int k_eff = sel_k(a, b, P);
   const int nch = (P + kChunk - 1) / kChunk;
   if (P <= 0) {
     if (w == 0 && t == 0) a.sel_count[b] = 0;

@@ -10,8 +10,7 @@
 
 #include "vegas_attn.h"
 #include "attn_common.h"
-#include "attn_mfma.h"
-#include "attn_valu.h"
+#include "launch.h"
 #include "select.h"
 #include "kv_append.h"
 #include "window_select.h"
@@ -54,25 +53,6 @@ vg_status supported_shape(const vg_shape *s) {
 
 bool use_mfma(const vg_shape *s) {
   return s->dtype == VG_DTYPE_BF16 && s->kernel != VG_KERNEL_VALU;
-}
-
-#ifndef VG_VERIFY_PF
-#define VG_VERIFY_PF 2   // tiles in flight per wave, D = 128
-#endif
-#ifndef VG_VERIFY_PF64
-#define VG_VERIFY_PF64 1  // D = 64: one tile in flight, two workgroups per CU
-#endif
-#ifndef VG_SPARSE_PF
-#define VG_SPARSE_PF 1   // tiles in flight per wave, sparse draft
-#endif
-
-// Tiles in flight per wave of the verify kernel: at D = 128 two (one when 3 or
-// 4 row tiles leave no registers for a second); at D = 64 one with two
-// workgroups per CU, and two when 4 row tiles make the merge area too large
-// for a second workgroup (one tile per wave in flight on one workgroup per
-// CU is too few bytes in flight to stream HBM).
-constexpr int verify_pf(int D, int NT) {
-  return D == 128 ? (NT <= 2 ? VG_VERIFY_PF : 1) : (NT <= 3 ? VG_VERIFY_PF64 : 2);
 }
 
 // Launch plan and workspace layout of one attention call.  Verify lists are
@@ -140,33 +120,6 @@ float effective_scale(const vg_shape *s) {
 }
 
 
-template <int D, int NT>
-void launch_mfma_nt(const AttnArgs &a, dim3 grid, hipStream_t st) {
-  if (a.sparse)
-    hipLaunchKernelGGL((attn_mfma_kernel<D, NT, VG_SPARSE_PF, true>), grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_mfma_kernel<D, NT, verify_pf(D, NT), false>), grid, dim3(kThreads), 0, st, a);
-}
-
-template <int D>
-void launch_mfma_d(int nt, const AttnArgs &a, dim3 grid, hipStream_t st) {
-  switch (nt) {
-    case 1: launch_mfma_nt<D, 1>(a, grid, st); break;
-    case 2: launch_mfma_nt<D, 2>(a, grid, st); break;
-    case 3: launch_mfma_nt<D, 3>(a, grid, st); break;
-    default: launch_mfma_nt<D, 4>(a, grid, st); break;
-  }
-}
-
-template <typename T, int D>
-void launch_valu_t(int mr, const AttnArgs &a, dim3 grid, hipStream_t st) {
-  switch (mr) {
-    case 16: hipLaunchKernelGGL((attn_valu_kernel<T, D, 16>), grid, dim3(kThreads), 0, st, a); break;
-    case 32: hipLaunchKernelGGL((attn_valu_kernel<T, D, 32>), grid, dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((attn_valu_kernel<T, D, 64>), grid, dim3(kThreads), 0, st, a); break;
-  }
-}
-
 template <int D>
 void launch_combine(int rpb, const AttnArgs &a, dim3 grid, hipStream_t st) {
   switch (rpb) {
@@ -191,14 +144,22 @@ vg_status launch_attention(const vg_shape *s, const AttnPlan &p, AttnArgs &a, ch
   a.rows = p.rows;
   const dim3 grid(p.workgroups);
   if (p.mfma) {
-    if (s->head_dim == 128) launch_mfma_d<128>(p.nt, a, grid, st);
-    else launch_mfma_d<64>(p.nt, a, grid, st);
-  } else if (s->dtype == VG_DTYPE_BF16) {
-    if (s->head_dim == 128) launch_valu_t<uint16_t, 128>(p.mr, a, grid, st);
-    else launch_valu_t<uint16_t, 64>(p.mr, a, grid, st);
+    if (s->head_dim == 128) {
+      if (a.sparse) launch_mfma128_sparse(p.nt, a, grid, st);
+      else launch_mfma128_verify(p.nt, a, grid, st);
+    } else {
+      if (a.sparse) launch_mfma64_sparse(p.nt, a, grid, st);
+      else launch_mfma64_verify(p.nt, a, grid, st);
+    }
   } else {
-    if (s->head_dim == 128) launch_valu_t<float, 128>(p.mr, a, grid, st);
-    else launch_valu_t<float, 64>(p.mr, a, grid, st);
+    const bool bf16 = s->dtype == VG_DTYPE_BF16;
+    if (s->head_dim == 128) {
+      if (bf16) launch_valu_bf16128(p.mr, a, grid, st);
+      else launch_valu_f32128(p.mr, a, grid, st);
+    } else {
+      if (bf16) launch_valu_bf1664(p.mr, a, grid, st);
+      else launch_valu_f3264(p.mr, a, grid, st);
+    }
   }
   // Rows per combine block: as many as leave each row enough partial groups
   // to load its (at most) np partials in one batch of 8 per thread.
@@ -470,6 +431,7 @@ vg_status vg_sparse_draft_attention(const vg_shape *shape, const void *q, int32_
   a.out = out;
   a.max_pages = shape->max_pages_per_seq;
   a.max_k = max_k;
+  a.max_tail = max_tail;
   a.nrows = n_q;
   a.gamma = 0;
   a.num_q_heads = shape->num_q_heads;

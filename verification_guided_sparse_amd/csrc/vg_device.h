@@ -153,7 +153,7 @@ struct AttnArgs {
   float *group;             // [B][Hkv][max_prefix] or null
   float *part_o;            // [parts][M][D], parts = workgroups + B * Hkv
   float *part_ml;           // [parts][M][2]
-  int32_t max_pages, max_k, max_prefix;
+  int32_t max_pages, max_k, max_prefix, max_tail;
   int32_t batch, nrows, gamma;
   int32_t num_q_heads, num_kv_heads, group_size, rows;  // rows = M = nrows * G
   int32_t workgroups;       // attention workgroups (grid size)
@@ -173,9 +173,10 @@ struct SeqList {
 __device__ __forceinline__ SeqList seq_list(const AttnArgs &a, int b) {
   SeqList s;
   if (a.sparse) {
-    s.cnt = a.sel_count[b];
+    // counts clamped to the list and tail capacities the launch was sized for
+    s.cnt = min(max(a.sel_count[b], 0), a.max_k);
     s.base = a.tail_start[b];
-    s.len = s.cnt + a.tail_len[b];
+    s.len = s.cnt + min(max(a.tail_len[b], 1), a.max_tail);
     s.p_export = 0;
   } else {
     s.cnt = 0;
