@@ -244,6 +244,33 @@ vg_status vg_sparse_draft_attention(const vg_shape *shape, const void *q, int32_
                                     size_t workspace_bytes, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as vg_sparse_draft_attention, with the same arguments except the
+ * workspace, which is a device array built into the library instead of a
+ * caller-provided buffer.
+ *
+ * The array is VG_NOALLOC_SCRATCH_BYTES (8 MiB) per GPU, held from the
+ * library's load until the process ends.  A call whose
+ * vg_sparse_draft_workspace_size exceeds it returns VG_ERR_WORKSPACE and
+ * launches nothing.  Nothing in this call allocates (no hipMalloc, hipFree
+ * or allocating library routine); its first call on a device looks up the
+ * array's device address (hipGetSymbolAddress) and keeps it for later calls.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * partial results: calls that may overlap on one GPU (different streams,
+ * concurrent host threads) race and must be ordered by the caller.  The
+ * array needs no zero state.  Results are bit-identical to
+ * vg_sparse_draft_attention's for the same inputs.
+ */
+#define VG_NOALLOC_SCRATCH_BYTES (8u << 20)
+vg_status vg_sparse_draft_attention_noalloc(const vg_shape *shape, const void *q, int32_t n_q,
+                                            const void *k_cache, const void *v_cache,
+                                            const int32_t *sel_slot, const int32_t *sel_count,
+                                            int32_t max_k, const int32_t *page_table,
+                                            const int32_t *tail_start, const int32_t *tail_len,
+                                            int32_t max_tail, float *out, void *stream);
+
+/*
  * Query-agnostic selection (Vegas section 1: sliding-window style selection
  * has little overhead but drafts less accurately; section 4 compares against
  * such a streaming baseline): the first n_sink prefix positions (attention

@@ -28,13 +28,15 @@ VG_KERNEL_MFMA = 2
 
 VG_TOPK_PREPASS_DONE = 1
 
+VG_NOALLOC_SCRATCH_BYTES = 8 << 20  # the built-in workspace of vg_sparse_draft_attention_noalloc
+
 # every symbol include/vegas_attn.h declares
 EXPORTS = (
     "vg_status_string", "vg_version", "vg_workspace_zero",
     "vg_verify_workspace_size", "vg_verify_attention", "vg_verify_attention_all_rows",
     "vg_aggregate_scores",
     "vg_topk_workspace_size", "vg_topk_select",
-    "vg_sparse_draft_workspace_size", "vg_sparse_draft_attention",
+    "vg_sparse_draft_workspace_size", "vg_sparse_draft_attention", "vg_sparse_draft_attention_noalloc",
     "vg_window_select", "vg_kv_append", "vg_advance_prefix",
 )
 
@@ -86,6 +88,7 @@ def lib():
         L.vg_topk_select.argtypes = [I32, P, I32, P, P, I32, P, I32, I32, P, P, P, I32, P, SZ, P]
         L.vg_sparse_draft_workspace_size.argtypes = [SP, I32, I32, I32, C.POINTER(SZ)]
         L.vg_sparse_draft_attention.argtypes = [SP, P, I32, P, P, P, P, I32, P, P, P, I32, P, P, SZ, P]
+        L.vg_sparse_draft_attention_noalloc.argtypes = [SP, P, I32, P, P, P, P, I32, P, P, P, I32, P, P]
         L.vg_window_select.argtypes = [I32, I32, P, P, I32, I32, P, I32, I32, P, P, P, P]
         L.vg_kv_append.argtypes = [SP, P, P, I32, P, P, P, P, P]
         L.vg_advance_prefix.argtypes = [I32, I32, P, P, P]
@@ -195,6 +198,14 @@ def vg_sparse_draft_attention(shape, q, n_q, k_cache, v_cache, sel_slot, sel_cou
         C.byref(shape), _ptr(q), int(n_q), _ptr(k_cache), _ptr(v_cache), _ptr(sel_slot),
         _ptr(sel_count), int(max_k), _ptr(page_table), _ptr(tail_start), _ptr(tail_len),
         int(max_tail), _ptr(out), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def vg_sparse_draft_attention_noalloc(shape, q, n_q, k_cache, v_cache, sel_slot, sel_count, max_k,
+                                      page_table, tail_start, tail_len, max_tail, out, stream=None):
+    _check("vg_sparse_draft_attention_noalloc", lib().vg_sparse_draft_attention_noalloc(
+        C.byref(shape), _ptr(q), int(n_q), _ptr(k_cache), _ptr(v_cache), _ptr(sel_slot),
+        _ptr(sel_count), int(max_k), _ptr(page_table), _ptr(tail_start), _ptr(tail_len),
+        int(max_tail), _ptr(out), _stream(stream)))
 
 
 def vg_window_select(batch, max_prefix, prefix_len, k, max_k, n_sink, page_table, page_size, max_pages,

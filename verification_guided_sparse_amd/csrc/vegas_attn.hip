@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "vegas_attn.h"
 #include "attn_common.h"
@@ -249,6 +250,76 @@ vg_status verify_impl(const vg_shape *shape, const void *q, const void *k_cache,
                           static_cast<hipStream_t>(stream));
 }
 
+// ---------------------------------------------------------------- scratch
+// Workspace of vg_sparse_draft_attention_noalloc: a file-scope device array,
+// one copy per GPU the library runs on, held until the process ends.  Host
+// code never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol): it looks up the device address once per device,
+// with that device current, and uses that pointer.
+constexpr size_t kScratchBytes = VG_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+vg_status scratch_on_current_device(void **ptr) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return VG_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return VG_ERR_HIP;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return VG_OK;
+}
+
+vg_status sparse_impl(const vg_shape *shape, const void *q, int32_t n_q,
+                      const void *k_cache, const void *v_cache,
+                      const int32_t *sel_slot, const int32_t *sel_count,
+                      int32_t max_k, const int32_t *page_table,
+                      const int32_t *tail_start, const int32_t *tail_len,
+                      int32_t max_tail, float *out, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  if (!valid_shape(shape) || n_q < 1 || max_k < 0 || max_tail < n_q) return VG_ERR_INVALID_ARG;
+  const void *req[] = {q, k_cache, v_cache, sel_count, page_table, tail_start, tail_len, out};
+  for (const void *p : req)
+    if (!p || !aligned16(p)) return VG_ERR_INVALID_ARG;
+  if (max_k > 0 && (!sel_slot || !aligned16(sel_slot))) return VG_ERR_INVALID_ARG;
+  const vg_status sup = supported_shape(shape);
+  if (sup != VG_OK) return sup;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  if (n_q * G > kMaxRows) return VG_ERR_UNSUPPORTED;
+  const AttnPlan p = plan_attention(shape, n_q, (long long)max_k + max_tail, true);
+  if (!p.ok) return VG_ERR_UNSUPPORTED;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < p.bytes) return VG_ERR_WORKSPACE;
+  AttnArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.page_table = page_table;
+  a.sel_slot = sel_slot;
+  a.sel_count = sel_count;
+  a.tail_start = tail_start;
+  a.tail_len = tail_len;
+  a.out = out;
+  a.max_pages = shape->max_pages_per_seq;
+  a.max_k = max_k;
+  a.max_tail = max_tail;
+  a.nrows = n_q;
+  a.gamma = 0;
+  a.num_q_heads = shape->num_q_heads;
+  a.num_kv_heads = shape->num_kv_heads;
+  a.group_size = G;
+  a.scale = effective_scale(shape);
+  a.scale_log2 = a.scale * kLog2e;
+  a.sparse = 1;
+  return launch_attention(shape, p, a, static_cast<char *>(workspace),
+                          static_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -407,41 +478,27 @@ vg_status vg_sparse_draft_attention(const vg_shape *shape, const void *q, int32_
                                     const int32_t *tail_start, const int32_t *tail_len,
                                     int32_t max_tail, float *out, void *workspace,
                                     size_t workspace_bytes, void *stream) {
-  if (!valid_shape(shape) || n_q < 1 || max_k < 0 || max_tail < n_q) return VG_ERR_INVALID_ARG;
-  const void *req[] = {q, k_cache, v_cache, sel_count, page_table, tail_start, tail_len, out};
-  for (const void *p : req)
-    if (!p || !aligned16(p)) return VG_ERR_INVALID_ARG;
-  if (max_k > 0 && (!sel_slot || !aligned16(sel_slot))) return VG_ERR_INVALID_ARG;
-  const vg_status sup = supported_shape(shape);
-  if (sup != VG_OK) return sup;
-  const int G = shape->num_q_heads / shape->num_kv_heads;
-  if (n_q * G > kMaxRows) return VG_ERR_UNSUPPORTED;
-  const AttnPlan p = plan_attention(shape, n_q, (long long)max_k + max_tail, true);
-  if (!p.ok) return VG_ERR_UNSUPPORTED;
-  if (!workspace || !aligned16(workspace) || workspace_bytes < p.bytes) return VG_ERR_WORKSPACE;
-  AttnArgs a{};
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.page_table = page_table;
-  a.sel_slot = sel_slot;
-  a.sel_count = sel_count;
-  a.tail_start = tail_start;
-  a.tail_len = tail_len;
-  a.out = out;
-  a.max_pages = shape->max_pages_per_seq;
-  a.max_k = max_k;
-  a.max_tail = max_tail;
-  a.nrows = n_q;
-  a.gamma = 0;
-  a.num_q_heads = shape->num_q_heads;
-  a.num_kv_heads = shape->num_kv_heads;
-  a.group_size = G;
-  a.scale = effective_scale(shape);
-  a.scale_log2 = a.scale * kLog2e;
-  a.sparse = 1;
-  return launch_attention(shape, p, a, static_cast<char *>(workspace),
-                          static_cast<hipStream_t>(stream));
+  return sparse_impl(shape, q, n_q, k_cache, v_cache, sel_slot, sel_count, max_k, page_table, tail_start,
+                     tail_len, max_tail, out, workspace, workspace_bytes, stream);
+}
+
+vg_status vg_sparse_draft_attention_noalloc(const vg_shape *shape, const void *q, int32_t n_q,
+                                            const void *k_cache, const void *v_cache,
+                                            const int32_t *sel_slot, const int32_t *sel_count,
+                                            int32_t max_k, const int32_t *page_table,
+                                            const int32_t *tail_start, const int32_t *tail_len,
+                                            int32_t max_tail, float *out, void *stream) {
+  // The size check comes first: a call that needs more than the array holds
+  // fails before anything touches the device.
+  size_t need = 0;
+  const vg_status q_st = vg_sparse_draft_workspace_size(shape, n_q, max_k, max_tail, &need);
+  if (q_st != VG_OK) return q_st;
+  if (need > kScratchBytes) return VG_ERR_WORKSPACE;
+  void *ws = nullptr;
+  const vg_status s_st = scratch_on_current_device(&ws);
+  if (s_st != VG_OK) return s_st;
+  return sparse_impl(shape, q, n_q, k_cache, v_cache, sel_slot, sel_count, max_k, page_table, tail_start,
+                     tail_len, max_tail, out, ws, kScratchBytes, stream);
 }
 
 vg_status vg_kv_append(const vg_shape *shape, const void *k_new, const void *v_new, int32_t n_new,
