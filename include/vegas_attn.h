@@ -209,6 +209,28 @@ vg_status vg_topk_select(int32_t batch, const float *scores, int32_t max_prefix,
                          int32_t *sel_pos, int32_t *sel_slot, int32_t *sel_count, int32_t flags,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Aggregation and exact top-k selection in one call: vg_aggregate_scores
+ * (scores from the exported logits, Vegas section 2.A objective restricted by
+ * section 2.B to the exported rows) followed by vg_topk_select (section 2.A:
+ * the k largest scores), with the same results as that pair of calls.
+ *
+ *   src, src_rows, src_heads, prefix_len, max_prefix, scores: as for
+ *       vg_aggregate_scores (scores[b][j] is written for j < P_b);
+ *   k, max_k, page_table, page_size, max_pages_per_seq, sel_pos, sel_slot,
+ *       sel_count: as for vg_topk_select;
+ *   workspace: sized by vg_topk_workspace_size(batch, max_prefix), zero-filled
+ *       once before first use (the call leaves it zero-filled again).
+ * With max_prefix <= 131072 and even, and page_size 16 (or sel_slot null), the
+ * whole selection runs in one kernel launch; otherwise in three.
+ */
+vg_status vg_aggregate_topk_select(int32_t batch, const float *src, int32_t src_rows, int32_t src_heads,
+                                   const int32_t *prefix_len, int32_t max_prefix, float *scores,
+                                   const int32_t *k, int32_t max_k, const int32_t *page_table,
+                                   int32_t page_size, int32_t max_pages_per_seq, int32_t *sel_pos,
+                                   int32_t *sel_slot, int32_t *sel_count, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
 /* --------------------------------------------------------- sparse draft */
 
 /* Workspace bytes vg_sparse_draft_attention needs. */

@@ -79,6 +79,25 @@ def _run_steps(c, kernel=None, pad=64):
         s_ref = oracle.aggregate(ref_src.astype(np.float64), c.prefix_len)
         _check(parity.score_gate(dc.host("scores"), s_ref, mask=mask_s), f"aggregate {src}")
 
+    # aggregation + top-k in one call on the oracle's exports: scores within
+    # the score tolerance, and the selection bit-exact against the oracle's
+    # top-k of the GPU's own fp32 scores
+    for src, ref_src in (("raw", logits_ref), ("group", group_ref)):
+        dc.select(src=src)
+        torch.cuda.synchronize()
+        s_gpu = dc.host("scores")
+        s_ref_src = oracle.aggregate(ref_src.astype(np.float32).astype(np.float64), c.prefix_len)
+        _check(parity.score_gate(s_gpu, s_ref_src, mask=mask_s), f"select {src} scores")
+        pr1, sr1, cr1 = oracle.topk(s_gpu.astype(np.float64), c.prefix_len, c.k, page_table=c.page_table,
+                                    max_k=dc.max_k)
+        cnt1 = dc.host("sel_count")
+        _check(parity.exact_gate(cnt1, cr1), f"select {src} count")
+        p1, q1 = dc.host("sel_pos"), dc.host("sel_slot")
+        for b in range(c.batch):
+            n = int(cr1[b])
+            _check(parity.exact_gate(p1[b, :n], pr1[b, :n]), f"select {src} positions seq {b}")
+            _check(parity.exact_gate(q1[b, :n], sr1[b, :n]), f"select {src} slots seq {b}")
+
     # top-k on the oracle's scores rounded to fp32: bit-exact against the oracle
     # taking the same decision in the same precision
     s_ref = oracle.aggregate(logits_ref, c.prefix_len)
@@ -424,6 +443,84 @@ def test_sparse_multi_row_draft(torch_cuda, name, n_q, kernel):
                                  _dev(tail_len, dev), R, out1, ws1, ws1_bytes)
     torch.cuda.synchronize()
     _check(parity.output_gate(out1.cpu().numpy(), o_ref[:, -1:]), "sparse one-row call, whole tail")
+
+
+def _topk_cases():
+    """(name, scores [B][mp] f32, P, k, max_k): edge and tie cases inside the
+    one-launch selection's range (max_prefix <= 2^17, even)."""
+    rng = np.random.default_rng(2024)
+    out = []
+    mp = 131072
+    # integer scores: tens of thousands of candidates share the threshold
+    # bin (past the LDS candidate cache), heavy ties at K*
+    s = rng.integers(0, 4, size=(2, mp)).astype(np.float32)
+    out.append(("heavy_ties", s, np.array([mp, 99_999], np.int32), np.array([40_000, 7], np.int32), 40_000))
+    # 1/64 grid: moderate ties
+    s = (np.round(rng.standard_normal((3, mp)) * 64) / 64).astype(np.float32)
+    out.append(("moderate_ties", s, np.array([mp, 70_001, 2049], np.int32),
+                np.array([5243, 3500, 2049], np.int32), 5243))
+    # continuous scores, ragged lengths around chunk edges, k = 0, k > P, P = 0, P = 1
+    s = rng.standard_normal((8, 8192)).astype(np.float32)
+    s[6, ::2] = -0.0
+    s[6, 1::2] = 0.0
+    out.append(("ragged_edges", s, np.array([8192, 2048, 2049, 0, 1, 4097, 3000, 6000], np.int32),
+                np.array([400, 0, 2049, 5, 1, 5000, 1500, 3], np.int32), 4097))
+    return out
+
+
+@pytest.mark.parametrize("case", [c[0] for c in _topk_cases()])
+def test_topk_paths_agree(torch_cuda, case):
+    """Every top-k path on the same fp32 scores, bit-exact against the oracle:
+    vg_topk_select in one launch, the three-pass path (vg_aggregate_scores with
+    the fused first pass, then VG_TOPK_PREPASS_DONE), and
+    vg_aggregate_topk_select on a one-row export holding the scores; each run
+    twice on one workspace (it must come back clean)."""
+    import torch
+    from verification_guided_sparse_amd import _binding as vg
+    name, s, P, k, max_k = next(c for c in _topk_cases() if c[0] == case)
+    B, mp = s.shape
+    _say(f"[parity] top-k paths {name} B={B} mp={mp}")
+    npg = -(-mp // 16)
+    rng = np.random.default_rng(7)
+    pt = np.stack([rng.permutation(npg) for _ in range(B)]).astype(np.int32)
+    # (the GPU gets k as is and clamps it to max_k; the oracle takes k <= max_k)
+    pr, sr, cr = oracle.topk(s.astype(np.float64), P, np.minimum(k, max_k), page_table=pt, max_k=max_k)
+    dev = dict(device="cuda")
+    ts = torch.from_numpy(s).cuda()
+    tP, tk, tpt = (torch.from_numpy(x).cuda() for x in (P, k, pt))
+    nbytes = vg.vg_topk_workspace_size(B, mp)
+    ws = torch.empty(nbytes, dtype=torch.uint8, **dev)
+    vg.vg_workspace_zero(ws, nbytes)
+    scores = torch.zeros(B, mp, dtype=torch.float32, **dev)
+
+    def run(path):
+        pos = torch.full((B, max_k), -1, dtype=torch.int32, **dev)
+        slot = torch.full((B, max_k), -1, dtype=torch.int32, **dev)
+        cnt = torch.full((B,), -1, dtype=torch.int32, **dev)
+        if path == "onepass":
+            vg.vg_topk_select(B, ts, mp, tP, tk, max_k, tpt, 16, npg, pos, slot, cnt, 0, ws, nbytes)
+        elif path == "threepass":
+            vg.vg_aggregate_scores(B, ts, 1, 1, tP, mp, scores, ws, nbytes)
+            vg.vg_topk_select(B, scores, mp, tP, tk, max_k, tpt, 16, npg, pos, slot, cnt,
+                              vg.VG_TOPK_PREPASS_DONE, ws, nbytes)
+        else:
+            vg.vg_aggregate_topk_select(B, ts, 1, 1, tP, mp, scores, tk, max_k, tpt, 16, npg, pos, slot, cnt,
+                                        ws, nbytes)
+        torch.cuda.synchronize()
+        return pos.cpu().numpy(), slot.cpu().numpy(), cnt.cpu().numpy()
+
+    for path in ("onepass", "threepass", "fused", "onepass", "fused"):
+        hp, hs, hc = run(path)
+        assert np.array_equal(hc, cr), path
+        for b in range(B):
+            n = int(cr[b])
+            assert np.array_equal(hp[b, :n], pr[b, :n]), (path, b)
+            assert np.array_equal(hs[b, :n], sr[b, :n]), (path, b)
+            assert np.all(hp[b, n:] == -1), (path, b)
+        if path != "onepass":  # the scores written by the aggregation are the input, exactly
+            sc = scores.cpu().numpy()
+            for b in range(B):
+                assert np.array_equal(sc[b, :P[b]], s[b, :P[b]]), (path, b)
 
 
 def test_topk_moderate_ties(torch_cuda):

@@ -1,0 +1,470 @@
+// select_split.h -- exact top-k selection (optionally with the score
+// aggregation) in two launches, for prefixes of up to kSplitMaxPrefix
+// positions.  Both kernels take one workgroup per chunk of 2048 positions of
+// each sequence.
+//
+//   stage    aggregate the chunk's scores from the export (or read them), key
+//            them (order-preserving uint32) and histogram the top 12 key bits
+//            in LDS.  Write the chunk's (key, position) pairs grouped by bin,
+//            highest bin first (`staged`), and per bin the number of the
+//            chunk's keys in that bin or above (`cnt_ge`, and every 64th bin
+//            of it transposed into `coarse`).
+//   resolve  every workgroup finds the sequence's k-th largest key K* by
+//            itself, from data that is small and shared by all of them: the
+//            bin b1 holding it (the sums over chunks of cnt_ge, searched 64
+//            bins at a time: coarse, then the 64-bin window), and K* within
+//            b1 from the candidates (bin b1: staged entries cnt_ge[b1 + 1] ..
+//            cnt_ge[b1] of every chunk) through two 10-bit histograms.  Then
+//            it writes its own chunk's selection: the staged entries above b1,
+//            the candidates above K*, and the keys equal to K* that the tie
+//            rule gives this chunk (lowest positions first, so earlier chunks
+//            take theirs first), in ascending position order at the chunk's
+//            offset, with their page-size-1 slots.
+//
+// No workgroup waits for another inside a kernel; the kernel boundary is the
+// only handoff.  The work that depends on one step (K*) is repeated by every
+// workgroup, so the chain of dependent steps after the boundary is short:
+// three rounds of loads (coarse counts, the window's counts, the candidates)
+// and LDS work.  The selected set does not depend on the order of staged
+// entries within a bin, so the result is deterministic although the staging
+// uses LDS atomics.
+//
+// Written around two properties of the hardware: a workgroup barrier waits
+// for every global load and store the wave has in flight, so the stage kernel
+// issues its global writes after its last barrier; and a load whose address
+// follows a data-dependent branch is not issued together with the others, so
+// each round of loads is computed without branches.
+#pragma once
+
+#include "select.h"
+
+namespace vg {
+
+constexpr int kStageThreads = 1024;
+constexpr int kStageWaves = kStageThreads / kWave;
+constexpr int kResolveThreads = 512;
+constexpr int kResolveWaves = kResolveThreads / kWave;
+constexpr int kSplitMaxPrefix = 1 << 17;
+constexpr int kSplitMaxChunks = kSplitMaxPrefix / kChunk;  // 64: one wave takes all chunks
+constexpr int kCntStride = kBins1 + 8;                     // u16 per chunk row of cnt_ge (16-byte rows)
+constexpr int kResolveCache = 6144;                        // candidates kept in LDS
+constexpr int kCandPiece = kWave;                          // candidates per read item
+
+// Workspace pieces of the two-launch selection (besides SelWs.cand, which
+// holds the staged pairs: chunk c at offset c * kChunk).
+struct StageWs {
+  uint16_t *cnt_ge;  // [B][chunks][kCntStride]: cnt_ge[c][bin] = keys of chunk c in bin or above
+  uint16_t *coarse;  // [B][64][kSplitMaxChunks]: cnt_ge[c][64 j] at [j][c]
+  int32_t chunks;    // chunk rows per sequence in cnt_ge
+};
+
+// Exclusive prefix sum over a block of NW waves; `total` receives the sum.
+template <int NW>
+__device__ __forceinline__ int block_scan_n(int v, int *sm, int &total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int x = wave_inclusive_scan(v);
+  if (lane == 63) sm[w] = x;
+  __syncthreads();
+  int pre = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int c = sm[i];
+    pre += (i < w) ? c : 0;
+    total += c;
+  }
+  __syncthreads();
+  return pre + x - v;
+}
+
+// Rank search by a block of NW waves over a histogram held PER bins per
+// thread, descending (thread t holds bins [nbins - PER (t + 1), nbins - PER t),
+// h[0] the highest): the bin holding the k-th largest key (1 <= k <= total),
+// the keys in higher bins (`above`) and the bin's own count.  Two barriers;
+// `wsum` (NW ints) and `res` (3 ints) of LDS must not be read by a later call
+// before its first barrier, so consecutive calls pass different `res`.
+template <int NW, int PER>
+__device__ __forceinline__ int find_bin_n(const uint32_t (&h)[PER], int nbins, int k, int *wsum, int *res,
+                                          int &above, int &count) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) local += (int)h[i];
+  const int x = wave_inclusive_scan(local);
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int pre = x - local;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) pre += (i < w) ? wsum[i] : 0;
+  if (pre < k && k <= pre + local) {  // exactly one thread
+    int run = pre;
+    bool done = false;
+    const int top = nbins - PER * t;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = (int)h[i];
+      if (!done && k <= run + c) {
+        res[0] = top - 1 - i;
+        res[1] = run;
+        res[2] = c;
+        done = true;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+  above = res[1];
+  count = res[2];
+  return res[0];
+}
+
+// ---------------------------------------------------------------- stage
+template <bool AGG>
+__global__ __launch_bounds__(kStageThreads, 2) void select_stage_kernel(SelArgs a, StageWs o) {
+  __shared__ uint32_t hist[kBins1];  // the histogram, then the counting-sort cursors
+  __shared__ u32x2 staged[kChunk];
+  __shared__ int wsum[kStageWaves];
+  const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
+  // loads first, before the length is known (positions below max_prefix are
+  // inside every row, and max_prefix is even)
+  const int j0 = w * kChunk + 2 * t;
+  const bool in_row = j0 < a.max_prefix;
+  const int P = sel_prefix(a, b);
+  f32x2 sc = {0.f, 0.f};
+  if (AGG) {
+    const int nrow = a.src_rows * a.src_heads;
+    const float *base = a.src + (size_t)b * nrow * a.max_prefix + j0;
+    constexpr int U = 8;
+    for (int r0 = 0; r0 < nrow; r0 += U) {
+      f32x2 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        v[u] = (in_row && r0 + u < nrow)
+                   ? __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(base + (size_t)(r0 + u) * a.max_prefix))
+                   : f32x2{0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < U; ++u) sc += v[u];
+    }
+  } else if (in_row) {
+    sc = *reinterpret_cast<const f32x2 *>(a.scores + (size_t)b * a.max_prefix + j0);
+  }
+  const int nch = (P + kChunk - 1) / kChunk;
+  if (w >= nch) return;
+  const bool v0 = j0 < P, v1 = j0 + 1 < P;
+  const uint32_t key0 = score_key(sc[0]), key1 = score_key(sc[1]);
+#pragma unroll
+  for (int i = 0; i < kBins1 / kStageThreads; ++i) hist[t + i * kStageThreads] = 0u;
+  __syncthreads();
+  if (v0) atomicAdd(&hist[key0 >> 20], 1u);
+  if (v1) atomicAdd(&hist[key1 >> 20], 1u);
+  __syncthreads();
+  // cnt_ge: thread t owns bins [4096 - 4 (t + 1), 4096 - 4 t), highest first
+  const int top = kBins1 - 4 * t;
+  uint32_t hh[4], ge[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hh[i] = hist[top - 1 - i];
+  {
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) local += (int)hh[i];
+    int total;
+    int run = block_scan_n<kStageWaves>(local, wsum, total);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      run += (int)hh[i];
+      ge[i] = (uint32_t)run;  // keys in bin top - 1 - i or above
+    }
+  }
+  // counting sort by bin, highest first: the cursor starts at the keys above the bin
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hist[top - 1 - i] = ge[i] - hh[i];
+  __syncthreads();
+  if (v0) staged[atomicAdd(&hist[key0 >> 20], 1u)] = u32x2{key0, (uint32_t)j0};
+  if (v1) staged[atomicAdd(&hist[key1 >> 20], 1u)] = u32x2{key1, (uint32_t)(j0 + 1)};
+  __syncthreads();
+  // global writes, after the last barrier
+  if (AGG) {
+    float *dst = a.scores_out + (size_t)b * a.max_prefix + j0;
+    if (v1) *reinterpret_cast<f32x2 *>(dst) = sc;
+    else if (v0) dst[0] = sc[0];
+  }
+  uint16_t *row = o.cnt_ge + ((size_t)b * o.chunks + w) * kCntStride;
+  *reinterpret_cast<u32x2 *>(row + top - 4) = u32x2{ge[3] | (ge[2] << 16), ge[1] | (ge[0] << 16)};
+  if (t == 0) row[kBins1] = 0;
+  if ((t & 15) == 15) {  // bin 64 j is the lowest of thread 1023 - 16 j's four bins
+    const int j = (kStageThreads - 1 - t) >> 4;
+    o.coarse[((size_t)b * 64 + j) * kSplitMaxChunks + w] = (uint16_t)ge[3];
+  }
+  const int n = min(P - w * kChunk, kChunk);
+  u32x2 *dst = a.ws.cand + (size_t)b * a.max_prefix + (size_t)w * kChunk;
+  if (2 * t + 1 < n)
+    *reinterpret_cast<u32x4 *>(dst + 2 * t) =
+        u32x4{staged[2 * t][0], staged[2 * t][1], staged[2 * t + 1][0], staged[2 * t + 1][1]};
+  else if (2 * t < n)
+    dst[2 * t] = staged[2 * t];
+}
+
+// ---------------------------------------------------------------- resolve
+struct ResolveSmem {
+  u32x2 cache[kResolveCache];  // the sequence's candidates, chunk by chunk
+  uint32_t h[kBins23];
+  int items[kSplitMaxChunks * (kChunk / kCandPiece)];  // candidate reads: chunk << 8 | piece
+  int32_t out[kChunk];         // this chunk's selected positions, ascending
+  int part[kResolveWaves][kWave];
+  int part64[kResolveWaves];
+  int g[kSplitMaxChunks + 1];
+  int hi[kSplitMaxChunks], lo[kSplitMaxChunks];
+  int cand_off[kSplitMaxChunks + 1];
+  int gt[kSplitMaxChunks], eq[kSplitMaxChunks];
+  uint32_t bm[kChunk / 32];   // this chunk's selected positions
+  uint32_t tie[kChunk / 32];  // this chunk's keys equal to K*
+  int32_t page[kChunk / kPageSize];
+  int meta[8];
+};
+
+__global__ __launch_bounds__(kResolveThreads, 2) void select_resolve_kernel(SelArgs a, StageWs o) {
+  __shared__ ResolveSmem S;
+  __shared__ int wsum[kResolveWaves];
+  __shared__ int res[4][4];
+  const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int P = sel_prefix(a, b);
+  const int kk = sel_k(a, b, P);
+  const int nch = (P + kChunk - 1) / kChunk;
+  if (w >= max(nch, 1)) return;
+  if (kk == 0) {  // (also P == 0)
+    if (w == 0 && t == 0) a.sel_count[b] = 0;
+    return;
+  }
+  const bool want_slots = a.sel_slot != nullptr;
+  const int c_ln = min(lane, nch - 1);
+  const bool live_ln = lane < nch;
+  // ---- round 1: G(64 j) = the sum over chunks of cnt_ge[c][64 j] (lane =
+  // chunk, wave v takes j = v + 8 m), and this chunk's page ids
+  {
+    const uint16_t *crow = o.coarse + (size_t)b * 64 * kSplitMaxChunks + c_ln;
+    uint32_t g1[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const uint32_t x = crow[(wave + kResolveWaves * m) * kSplitMaxChunks];
+      g1[m] = live_ln ? x : 0u;
+    }
+    int pid = 0;
+    if (want_slots && t < kChunk / kPageSize)
+      pid = a.page_table[(size_t)b * a.max_pages + min(w * (kChunk / kPageSize) + t, a.max_pages - 1)];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int sum = __builtin_amdgcn_readlane(wave_inclusive_scan((int)g1[m]), 63);
+      if (lane == 0) S.g[wave + kResolveWaves * m] = sum;
+    }
+    if (t < kChunk / kPageSize) S.page[t] = pid;
+    if (t < kChunk / 32) {
+      S.bm[t] = 0u;
+      S.tie[t] = 0u;
+    }
+    if (t < kSplitMaxChunks) {
+      S.gt[t] = 0;
+      S.eq[t] = 0;
+    }
+    S.h[t] = 0u;
+    S.h[t + kResolveThreads] = 0u;
+  }
+  __syncthreads();
+  // ---- round 2: G at the 65 bins base2 + l of the window the first round
+  // found (lane = bin, wave v takes chunks v + 8 m; one line per load)
+  const int istar = 63 - (int)__builtin_clzll(__builtin_amdgcn_ballot_w64(S.g[lane] >= kk));  // G(0) = P >= kk
+  const int base2 = 64 * istar;
+  uint32_t f[8], f64[8];
+  {
+    const uint16_t *rows = o.cnt_ge + (size_t)b * o.chunks * kCntStride;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int c = min(wave + kResolveWaves * m, nch - 1);
+      const bool in = wave + kResolveWaves * m < nch;
+      const uint32_t x = rows[(size_t)c * kCntStride + base2 + lane];
+      const uint32_t y = rows[(size_t)c * kCntStride + min(base2 + 64, kBins1)];
+      f[m] = in ? x : 0u;
+      f64[m] = in ? y : 0u;
+    }
+    int s = 0, s64 = 0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      s += (int)f[m];
+      s64 += (int)f64[m];
+    }
+    S.part[wave][lane] = s;
+    if (lane == 0) S.part64[wave] = s64;
+  }
+  __syncthreads();  // (also: every wave has read the first round's sums)
+  if (wave == 0) {
+    int g2 = 0, g64 = 0;
+#pragma unroll
+    for (int q = 0; q < kResolveWaves; ++q) {
+      g2 += S.part[q][lane];
+      g64 += S.part64[q];
+    }
+    const int jb = 63 - (int)__builtin_clzll(__builtin_amdgcn_ballot_w64(g2 >= kk));  // G(base2) >= kk
+    const int above = jb < 63 ? __shfl(g2, jb + 1) : g64;
+    if (lane == 0) {
+      S.meta[0] = jb;
+      S.meta[1] = above;
+    }
+  }
+  __syncthreads();
+  const int jb = S.meta[0];
+  const uint32_t b1 = (uint32_t)(base2 + jb);
+  const int k1 = kk - S.meta[1];  // rank of K* inside bin b1 (>= 1)
+  // each chunk's counts at b1 and b1 + 1, from the loading lanes' registers
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int c = wave + kResolveWaves * m;
+    if (c < nch) {
+      if (lane == jb) S.hi[c] = (int)f[m];
+      if (lane == jb + 1) S.lo[c] = (int)f[m];
+      if (jb == 63 && lane == 0) S.lo[c] = (int)f64[m];
+    }
+  }
+  __syncthreads();
+  // wave 0: candidates before each chunk, and the candidate read items
+  if (wave == 0) {
+    const int nc = live_ln ? S.hi[lane] - S.lo[lane] : 0;
+    const int cd = wave_inclusive_scan(nc);
+    if (live_ln) S.cand_off[lane] = cd - nc;
+    if (lane == 63) S.cand_off[nch] = cd;
+    const int np = (nc + kCandPiece - 1) / kCandPiece;
+    const int io = wave_inclusive_scan(np);
+    for (int r = 0; r < np; ++r) S.items[io - np + r] = (lane << 8) | r;
+    if (lane == 63) S.meta[2] = io;
+  }
+  __syncthreads();
+  const int n_cand = S.cand_off[nch];
+  const bool cached = n_cand <= kResolveCache;
+  const u32x2 *stg = a.ws.cand + (size_t)b * a.max_prefix;
+  // ---- round 3: this chunk's entries above b1 (their bits), and every
+  // candidate into the LDS cache (wave v takes items v, v + 8, ...)
+  {
+    const int lo_own = S.lo[w];
+    const int n_items = cached ? S.meta[2] : 0;
+    constexpr int Q = 4;
+    for (int r0 = 0;; r0 += Q) {
+      const int it_base = wave + kResolveWaves * r0;
+      const int own_base = kResolveThreads * r0;
+      if (it_base >= n_items && own_base >= lo_own) break;  // (wave-uniform for items; own work is per thread)
+      u32x2 v[Q], u[Q];
+      int c_of[Q], i_of[Q];
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int it = it_base + kResolveWaves * q;
+        const int item = S.items[min(it, max(n_items - 1, 0))];
+        const int c = item >> 8, i = kCandPiece * (item & 255) + lane;
+        const bool ok = it < n_items && i < S.hi[c] - S.lo[c];
+        c_of[q] = ok ? c : -1;
+        i_of[q] = i;
+        v[q] = stg[ok ? (size_t)c * kChunk + S.lo[c] + i : 0];
+        const int e = own_base + kResolveThreads * q + t;
+        u[q] = stg[(size_t)w * kChunk + min(e, max(lo_own - 1, 0))];
+      }
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        if (c_of[q] >= 0) S.cache[S.cand_off[c_of[q]] + i_of[q]] = v[q];
+        const int e = own_base + kResolveThreads * q + t;
+        if (e < lo_own) {
+          const int p = (int)u[q][1] - w * kChunk;
+          atomicOr(&S.bm[p >> 5], 1u << (p & 31));
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // candidate i (0 <= i < n_cand) of the sequence
+  auto cand = [&](int i) -> u32x2 {
+    if (cached) return S.cache[i];
+    int c = 0;
+    while (S.cand_off[c + 1] <= i) ++c;
+    return stg[(size_t)c * kChunk + S.lo[c] + (i - S.cand_off[c])];
+  };
+  // ---- K* from the candidates: bits [10, 20), then [0, 10)
+  for (int i = t; i < n_cand; i += kResolveThreads) atomicAdd(&S.h[(cand(i)[0] >> 10) & 1023u], 1u);
+  __syncthreads();
+  uint32_t hb[2] = {S.h[kBins23 - 1 - 2 * t], S.h[kBins23 - 2 - 2 * t]};
+  int above2, n_b2;
+  const uint32_t b2 = (uint32_t)find_bin_n<kResolveWaves, 2>(hb, kBins23, k1, wsum, res[0], above2, n_b2);
+  const int k2 = k1 - above2;
+  const uint32_t pre22 = (b1 << 10) | b2;
+  S.h[kBins23 - 1 - 2 * t] = 0u;  // each thread clears the bins it read
+  S.h[kBins23 - 2 - 2 * t] = 0u;
+  __syncthreads();
+  for (int i = t; i < n_cand; i += kResolveThreads) {
+    const uint32_t key = cand(i)[0];
+    if ((key >> 10) == pre22) atomicAdd(&S.h[key & 1023u], 1u);
+  }
+  __syncthreads();
+  hb[0] = S.h[kBins23 - 1 - 2 * t];
+  hb[1] = S.h[kBins23 - 2 - 2 * t];
+  int above3, n_eq;
+  const uint32_t b3 = (uint32_t)find_bin_n<kResolveWaves, 2>(hb, kBins23, k2, wsum, res[1], above3, n_eq);
+  const uint32_t kstar = (pre22 << 10) | b3;
+  const int ties = k2 - above3;  // keys equal to K* to keep, lowest positions first
+  // ---- per chunk: candidates above and equal to K* (a candidate's chunk is
+  // its position / 2048); this chunk's own go to its bitmaps
+  for (int i = t; i < n_cand; i += kResolveThreads) {
+    const u32x2 e = cand(i);
+    const int c = (int)(e[1] >> 11);
+    if (e[0] > kstar) {
+      atomicAdd(&S.gt[c], 1);
+      if (c == w) atomicOr(&S.bm[(e[1] & (kChunk - 1)) >> 5], 1u << (e[1] & 31));
+    } else if (e[0] == kstar) {
+      atomicAdd(&S.eq[c], 1);
+      if (c == w) atomicOr(&S.tie[(e[1] & (kChunk - 1)) >> 5], 1u << (e[1] & 31));
+    }
+  }
+  __syncthreads();
+  // ---- wave 0: the chunk's output offset and its share of the ties, then its
+  // positions in order (lane = bitmap word of 32 positions)
+  if (wave == 0) {
+    const int eq = live_ln ? S.eq[lane] : 0;
+    const int eq_before = wave_inclusive_scan(eq) - eq;
+    const int take = min(eq, max(0, ties - eq_before));  // ties taken in this chunk
+    const int sel = live_ln ? S.lo[lane] + S.gt[lane] + take : 0;
+    const int off = wave_inclusive_scan(sel) - sel;
+    const int my_off = __shfl(off, w), my_take = __shfl(take, w);
+    // this chunk's ties: the first my_take tie bits in position order
+    uint32_t tw = S.tie[lane];
+    const int tc = __popc(tw);
+    int rank = wave_inclusive_scan(tc) - tc;
+    uint32_t x = tw;
+    while (x) {
+      const uint32_t bit = x & (~x + 1u);
+      if (rank >= my_take) tw &= ~bit;
+      ++rank;
+      x &= x - 1u;
+    }
+    uint32_t word = S.bm[lane] | tw;
+    const int cnt = __popc(word);
+    int idx = wave_inclusive_scan(cnt) - cnt;
+    while (word) {
+      const int bit = __ffs(word) - 1;
+      word &= word - 1u;
+      S.out[idx++] = w * kChunk + 32 * lane + bit;
+    }
+    if (lane == 63) {
+      S.meta[3] = my_off;
+      S.meta[4] = idx;  // this chunk's selected count
+    }
+  }
+  __syncthreads();
+  const int my_off = S.meta[3], n_own = S.meta[4];
+  int32_t *pos_row = a.sel_pos + (size_t)b * a.max_k;
+  int32_t *slot_row = want_slots ? a.sel_slot + (size_t)b * a.max_k : nullptr;
+  for (int j = t; j < n_own; j += kResolveThreads) {
+    const int idx = my_off + j;
+    if (idx < a.max_k) {
+      const int pos = S.out[j];
+      pos_row[idx] = pos;
+      if (want_slots) slot_row[idx] = S.page[(pos & (kChunk - 1)) >> 4] * kPageSize + (pos & (kPageSize - 1));
+    }
+  }
+  if (w == 0 && t == 0) a.sel_count[b] = kk;
+}
+
+}  // namespace vg

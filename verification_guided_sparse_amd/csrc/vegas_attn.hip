@@ -13,6 +13,7 @@
 #include "attn_common.h"
 #include "launch.h"
 #include "select.h"
+#include "select_split.h"
 #include "kv_append.h"
 #include "window_select.h"
 
@@ -177,19 +178,40 @@ vg_status launch_attention(const vg_shape *s, const AttnPlan &p, AttnArgs &a, ch
 
 // ---------------------------------------------------------------- topk workspace
 struct SelPlan {
-  size_t off_hist1, off_hist2, off_state, off_above, off_ncand, off_cand, bytes;
+  size_t off_hist1, off_hist2, off_state, off_above, off_ncand, off_cand, off_cntge, off_coarse, bytes;
+  int chunks;  // chunks of kChunk positions per sequence
 };
+
+// Two-launch selection (select_split.h): prefixes up to kSplitMaxPrefix with
+// even rows (8-byte score loads), and slots through 16-token pages.
+bool split_ok(int batch, int max_prefix, bool slots, int page_size) {
+  return max_prefix <= kSplitMaxPrefix && max_prefix % 2 == 0 && batch <= 65535 &&
+         (!slots || page_size == kPageSize);
+}
 
 SelPlan plan_select(int batch, int max_prefix) {
   SelPlan p{};
+  p.chunks = ceil_div(max_prefix > 0 ? max_prefix : 1, kChunk);
   p.off_hist1 = 0;
   p.off_hist2 = align_up((size_t)batch * kBins1 * sizeof(uint32_t));
   p.off_state = p.off_hist2 + align_up((size_t)batch * kBins23 * sizeof(uint32_t));
   p.off_above = p.off_state + align_up((size_t)batch * 4 * sizeof(int32_t));
   p.off_ncand = p.off_above + align_up((size_t)batch * kMaxChunks * sizeof(int32_t));
   p.off_cand = p.off_ncand + align_up((size_t)batch * kMaxChunks * sizeof(int32_t));
-  p.bytes = p.off_cand + align_up((size_t)batch * (size_t)(max_prefix > 0 ? max_prefix : 1) * 8);
+  p.off_cntge = p.off_cand + align_up((size_t)batch * (size_t)(max_prefix > 0 ? max_prefix : 1) * 8);
+  const bool split = max_prefix <= kSplitMaxPrefix;
+  p.off_coarse = p.off_cntge + (split ? align_up((size_t)batch * p.chunks * kCntStride * sizeof(uint16_t)) : 0);
+  p.bytes = p.off_coarse + (split ? align_up((size_t)batch * 64 * kSplitMaxChunks * sizeof(uint16_t)) : 0);
   return p;
+}
+
+StageWs stage_ws(const SelPlan &p, void *ws) {
+  char *c = static_cast<char *>(ws);
+  StageWs o;
+  o.cnt_ge = reinterpret_cast<uint16_t *>(c + p.off_cntge);
+  o.coarse = reinterpret_cast<uint16_t *>(c + p.off_coarse);
+  o.chunks = p.chunks;
+  return o;
 }
 
 SelWs sel_ws(const SelPlan &p, void *ws) {
@@ -450,10 +472,64 @@ vg_status vg_topk_select(int32_t batch, const float *scores, int32_t max_prefix,
   a.ws = sel_ws(p, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid(ceil_div(max_prefix > 0 ? max_prefix : 1, kChunk), batch);
+  if (!(flags & VG_TOPK_PREPASS_DONE) && split_ok(batch, max_prefix, sel_slot != nullptr, page_size)) {
+    const StageWs o = stage_ws(p, workspace);
+    hipLaunchKernelGGL((select_stage_kernel<false>), grid, dim3(kStageThreads), 0, st, a, o);
+    hipLaunchKernelGGL(select_resolve_kernel, grid, dim3(kResolveThreads), 0, st, a, o);
+    return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
+  }
   if (!(flags & VG_TOPK_PREPASS_DONE))
     hipLaunchKernelGGL((select_pass1_kernel<false, true>), grid, dim3(kP1Threads), 0, st, a);
   hipLaunchKernelGGL(select_pass2_kernel, grid, dim3(kSelThreads), 0, st, a);
   hipLaunchKernelGGL(select_pass3_kernel, grid, dim3(kSelThreads), 0, st, a);
+  return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
+}
+
+vg_status vg_aggregate_topk_select(int32_t batch, const float *src, int32_t src_rows, int32_t src_heads,
+                                   const int32_t *prefix_len, int32_t max_prefix, float *scores,
+                                   const int32_t *k, int32_t max_k, const int32_t *page_table,
+                                   int32_t page_size, int32_t max_pages_per_seq, int32_t *sel_pos,
+                                   int32_t *sel_slot, int32_t *sel_count, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  if (batch < 1 || src_rows < 1 || src_heads < 1 || max_prefix < 0 || max_k < 0) return VG_ERR_INVALID_ARG;
+  const void *req[] = {src, prefix_len, scores, k, sel_pos, sel_count};
+  for (const void *ptr : req)
+    if (!ptr || !aligned16(ptr)) return VG_ERR_INVALID_ARG;
+  if (sel_slot && (!aligned16(sel_slot) || !page_table || !aligned16(page_table) || page_size < 1 ||
+                   max_pages_per_seq < 1 || ceil_div(max_prefix, page_size) > max_pages_per_seq))
+    return VG_ERR_INVALID_ARG;
+  if (max_prefix > kMaxSelectPrefix) return VG_ERR_UNSUPPORTED;
+  const SelPlan p = plan_select(batch, max_prefix);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < p.bytes) return VG_ERR_WORKSPACE;
+  SelArgs a{};
+  a.batch = batch;
+  a.max_prefix = max_prefix;
+  a.max_k = max_k;
+  a.prefix_len = prefix_len;
+  a.k = k;
+  a.scores = scores;
+  a.scores_out = scores;
+  a.src = src;
+  a.src_rows = src_rows;
+  a.src_heads = src_heads;
+  a.page_table = page_table;
+  a.page_size = page_size;
+  a.max_pages = max_pages_per_seq;
+  a.sel_pos = sel_pos;
+  a.sel_slot = sel_slot;
+  a.sel_count = sel_count;
+  a.ws = sel_ws(p, workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(ceil_div(max_prefix > 0 ? max_prefix : 1, kChunk), batch);
+  if (split_ok(batch, max_prefix, sel_slot != nullptr, page_size)) {
+    const StageWs o = stage_ws(p, workspace);
+    hipLaunchKernelGGL((select_stage_kernel<true>), grid, dim3(kStageThreads), 0, st, a, o);
+    hipLaunchKernelGGL(select_resolve_kernel, grid, dim3(kResolveThreads), 0, st, a, o);
+  } else {
+    hipLaunchKernelGGL((select_pass1_kernel<true, true>), grid, dim3(kP1Threads), 0, st, a);
+    hipLaunchKernelGGL(select_pass2_kernel, grid, dim3(kSelThreads), 0, st, a);
+    hipLaunchKernelGGL(select_pass3_kernel, grid, dim3(kSelThreads), 0, st, a);
+  }
   return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
 }
 

@@ -100,14 +100,17 @@ class DeviceCase:
         fn(self.shape, self.q, self.k_cache, self.v_cache, self.page_table, self.prefix_len, self.max_prefix,
            self.gamma, self.out, logits, group, self.ws_verify, self.ws_verify_bytes, stream)
 
+    def _export(self, src):
+        """(buffer, rows, heads) of an export: "raw" (two rows), "raw_all" (every row) or "group"."""
+        if src == "raw":
+            return self.logits, 2, self.Hq
+        if src == "raw_all":
+            return self.logits_all, self.R, self.Hq
+        return self.group, 1, self.Hkv
+
     def aggregate(self, src="raw", fuse_prepass=False, stream=None):
         """src: "raw" (two rows), "raw_all" (every row) or "group"."""
-        if src == "raw":
-            t, rows, heads = self.logits, 2, self.Hq
-        elif src == "raw_all":
-            t, rows, heads = self.logits_all, self.R, self.Hq
-        else:
-            t, rows, heads = self.group, 1, self.Hkv
+        t, rows, heads = self._export(src)
         ws = self.ws_select if fuse_prepass else None
         vg.vg_aggregate_scores(self.B, t, rows, heads, self.prefix_len, self.max_prefix, self.scores,
                                ws, self.ws_select_bytes if fuse_prepass else 0, stream)
@@ -118,6 +121,15 @@ class DeviceCase:
                           self.prefix_len, self.k, self.max_k, self.page_table, self.case.page_size,
                           self.max_pages, self.sel_pos, self.sel_slot, self.sel_count, flags,
                           self.ws_select, self.ws_select_bytes, stream)
+
+    def select(self, src="group", stream=None):
+        """Aggregation and top-k in one call (vg_aggregate_topk_select): scores, then
+        the selection into sel_pos / sel_slot / sel_count.  src as for aggregate()."""
+        t, rows, heads = self._export(src)
+        vg.vg_aggregate_topk_select(self.B, t, rows, heads, self.prefix_len, self.max_prefix, self.scores,
+                                    self.k, self.max_k, self.page_table, self.case.page_size, self.max_pages,
+                                    self.sel_pos, self.sel_slot, self.sel_count, self.ws_select,
+                                    self.ws_select_bytes, stream)
 
     def window(self, n_sink=4, stream=None):
         """Query-agnostic selection into the same buffers as topk(): n_sink sink
@@ -167,8 +179,7 @@ class DeviceCase:
         """One pass of the whole path: verify (+export), aggregate, top-k, gamma draft steps."""
         self.verify(export=export, rows=rows, stream=stream)
         src = "group" if export == "group" else ("raw" if rows == "two" else "raw_all")
-        self.aggregate(src=src, fuse_prepass=True, stream=stream)
-        self.topk(prepass_done=True, stream=stream)
+        self.select(src=src, stream=stream)
         for s in range(self.gamma):
             self.sparse(step=s, stream=stream)
 
