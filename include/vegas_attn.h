@@ -231,6 +231,30 @@ vg_status vg_aggregate_topk_select(int32_t batch, const float *src, int32_t src_
                                    int32_t *sel_slot, int32_t *sel_count, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
+/*
+ * Verification attention with the group export, then aggregation and exact
+ * top-k selection (Vegas section 2: verification computes every entry's
+ * logits; section 2.B: the first draft token's and the bonus token's are
+ * collected; section 2.A: the k positions with the largest summed logits are
+ * selected), with the same results as
+ *     vg_verify_attention(..., logits = NULL, group_scores, ...)
+ *     vg_aggregate_topk_select(batch, group_scores, 1, Hkv, prefix_len, max_prefix, scores, ...).
+ * The selection's first step runs in the same launch as the verify combine.
+ *
+ *   shape .. out, verify_ws: as for vg_verify_attention (group_scores must be
+ *       non-null; raw logits are not exported);
+ *   scores, k, max_k, sel_pos, sel_slot, sel_count: as for
+ *       vg_aggregate_topk_select, with page_table, page_size and
+ *       max_pages_per_seq taken from the verify arguments;
+ *   select_ws: sized by vg_topk_workspace_size(batch, max_prefix), zero-filled
+ *       once before first use.
+ */
+vg_status vg_verify_select(const vg_shape *shape, const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *page_table, const int32_t *prefix_len, int32_t max_prefix, int32_t gamma,
+                           float *out, float *group_scores, float *scores, const int32_t *k, int32_t max_k,
+                           int32_t *sel_pos, int32_t *sel_slot, int32_t *sel_count, void *verify_ws,
+                           size_t verify_ws_bytes, void *select_ws, size_t select_ws_bytes, void *stream);
+
 /* --------------------------------------------------------- sparse draft */
 
 /* Workspace bytes vg_sparse_draft_attention needs. */

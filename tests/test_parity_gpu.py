@@ -657,6 +657,50 @@ def test_graph_replay_matches_eager(torch_cuda):
             assert np.array_equal(got["sel_slot"][b, :k], ref["sel_slot"][b, :k]), (rep, b)
 
 
+@pytest.mark.parametrize("name,pad", [("c2_small", 64), ("c4_small", 64), ("c5_small", 64), ("short_prefixes", 64),
+                                      ("c1_tiny", 64), ("c3_small", 64), ("c4_small", 1), ("c5_small", 1)])
+def test_verify_select_matches_separate_calls(torch_cuda, name, pad):
+    """vg_verify_select (verify with the group export, aggregation and top-k,
+    the selection's staging in the combine's launch) gives bit for bit what
+    vg_verify_attention followed by vg_aggregate_topk_select gives -- also on
+    unpadded rows, where it runs the separate calls' kernels -- and the chain
+    passes the oracle's gates."""
+    import torch
+    from verification_guided_sparse_amd.runner import DeviceCase
+    c = synth.make_case(SMALL[name]())
+    _say(f"[parity] verify_select {name} pad={pad}")
+    dc = DeviceCase(c, pad=pad)
+    dc.verify(export="group")
+    dc.select(src="group")
+    torch.cuda.synchronize()
+    names = ("out", "group", "scores", "sel_pos", "sel_slot", "sel_count")
+    ref = {n: dc.host(n).copy() for n in names}
+    for n in ("out", "group", "scores"):
+        getattr(dc, n).fill_(float("nan"))
+    for n in ("sel_pos", "sel_slot", "sel_count"):
+        getattr(dc, n).fill_(-7)
+    for rep in range(2):
+        dc.verify_select()
+        torch.cuda.synchronize()
+        for n in names:
+            got = dc.host(n)
+            if n in ("sel_pos", "sel_slot"):
+                for b in range(c.batch):
+                    m = int(ref["sel_count"][b])
+                    assert np.array_equal(got[b, :m], ref[n][b, :m]), (n, b, rep)
+            elif n in ("group", "scores"):
+                mask = _rows_mask(c, (c.num_kv_heads,) if n == "group" else ())
+                assert np.array_equal(np.where(mask, got, 0), np.where(mask, ref[n], 0)), (n, rep)
+            else:
+                assert np.array_equal(got, ref[n]), (n, rep)
+    out_ref, logits_ref, group_ref = _oracle_all(c)
+    s_ref = oracle.aggregate(logits_ref, c.prefix_len)
+    _check(parity.output_gate(dc.host("out"), out_ref), "verify_select out")
+    _check(parity.score_gate(dc.host("scores"), s_ref, mask=_rows_mask(c, ())), "verify_select scores")
+    _check(parity.topk_gate(dc.host("sel_pos"), dc.host("sel_count"), s_ref, c.prefix_len, c.k),
+           "verify_select topk")
+
+
 @pytest.mark.parametrize("name", ["c2_small", "c5_small", "short_prefixes", "gamma0", "c1_tiny"])
 def test_full_collection_parity(torch_cuda, name):
     """All-rows export (the objective over every verify row): logits of every row,

@@ -35,7 +35,7 @@ EXPORTS = (
     "vg_status_string", "vg_version", "vg_workspace_zero",
     "vg_verify_workspace_size", "vg_verify_attention", "vg_verify_attention_all_rows",
     "vg_aggregate_scores",
-    "vg_topk_workspace_size", "vg_topk_select", "vg_aggregate_topk_select",
+    "vg_topk_workspace_size", "vg_topk_select", "vg_aggregate_topk_select", "vg_verify_select",
     "vg_sparse_draft_workspace_size", "vg_sparse_draft_attention", "vg_sparse_draft_attention_noalloc",
     "vg_window_select", "vg_kv_append", "vg_advance_prefix",
 )
@@ -86,6 +86,7 @@ def lib():
         L.vg_aggregate_scores.argtypes = [I32, P, I32, I32, P, I32, P, P, SZ, P]
         L.vg_topk_workspace_size.argtypes = [I32, I32, C.POINTER(SZ)]
         L.vg_topk_select.argtypes = [I32, P, I32, P, P, I32, P, I32, I32, P, P, P, I32, P, SZ, P]
+        L.vg_verify_select.argtypes = [SP, P, P, P, P, P, I32, I32, P, P, P, P, I32, P, P, P, P, SZ, P, SZ, P]
         L.vg_aggregate_topk_select.argtypes = [I32, P, I32, I32, P, I32, P, P, I32, P, I32, I32, P, P, P, P,
                                                SZ, P]
         L.vg_sparse_draft_workspace_size.argtypes = [SP, I32, I32, I32, C.POINTER(SZ)]
@@ -193,6 +194,16 @@ def vg_aggregate_topk_select(batch, src, src_rows, src_heads, prefix_len, max_pr
         int(batch), _ptr(src), int(src_rows), int(src_heads), _ptr(prefix_len), int(max_prefix), _ptr(scores),
         _ptr(k), int(max_k), _ptr(page_table), int(page_size), int(max_pages), _ptr(sel_pos), _ptr(sel_slot),
         _ptr(sel_count), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def vg_verify_select(shape, q, k_cache, v_cache, page_table, prefix_len, max_prefix, gamma, out, group_scores,
+                     scores, k, max_k, sel_pos, sel_slot, sel_count, verify_ws, verify_ws_bytes, select_ws,
+                     select_ws_bytes, stream=None):
+    _check("vg_verify_select", lib().vg_verify_select(
+        C.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(prefix_len), int(max_prefix),
+        int(gamma), _ptr(out), _ptr(group_scores), _ptr(scores), _ptr(k), int(max_k), _ptr(sel_pos),
+        _ptr(sel_slot), _ptr(sel_count), _ptr(verify_ws), int(verify_ws_bytes), _ptr(select_ws),
+        int(select_ws_bytes), _stream(stream)))
 
 
 def vg_sparse_draft_workspace_size(shape: VgShape, n_q: int, max_k: int, max_tail: int) -> int:

@@ -206,7 +206,7 @@ __host__ __device__ inline bool share_meets(const Pre &pre, int batch, int Hkv, 
 // flight together, keeping an online (max, denominator, sum) state; the
 // groups' states are then merged through LDS.
 template <int D, int RPB>
-__global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
+__device__ __forceinline__ void combine_block(const AttnArgs &a, int bx, int g, int b) {
   constexpr int C = D / 4;              // float4 columns of a row
   constexpr int TPR = kThreads / RPB;   // threads per row
   constexpr int SP = TPR / C;           // partial groups per row
@@ -217,9 +217,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
   __shared__ float sm_m[kThreads];
   __shared__ float sm_d[RPB * SP];
   __shared__ f32x4 sm_o[kThreads];
-  const int g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int t = threadIdx.x;
   const int rg = t / TPR, tr = t % TPR;  // this thread's row in the block, its index in the row
-  const int row = blockIdx.x * RPB + rg;
+  const int row = bx * RPB + rg;
   const int Hkv = a.num_kv_heads, W = a.workgroups;
   const bool fixed = a.split_tokens > 0;
   const int seg = b * Hkv + g, M = a.rows;
@@ -347,6 +347,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
     *reinterpret_cast<f32x4 *>(a.out + (((size_t)b * a.nrows + qr) * a.num_q_heads + h) * D + 4 * tr) =
         acc * (1.0f / den);
   }
+}
+
+// Combine blocks of one or more rows per (KV head, sequence): grid
+// (ceil(M / RPB), Hkv, B).
+template <int D, int RPB>
+__global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
+  combine_block<D, RPB>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // x of the first active lane (a wave-uniform value the compiler may keep in a

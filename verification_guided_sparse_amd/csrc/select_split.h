@@ -119,89 +119,123 @@ __device__ __forceinline__ int find_bin_n(const uint32_t (&h)[PER], int nbins, i
 }
 
 // ---------------------------------------------------------------- stage
-template <bool AGG>
-__global__ __launch_bounds__(kStageThreads, 2) void select_stage_kernel(SelArgs a, StageWs o) {
+// One chunk (w) of sequence b by a block of NT threads, 2048 / NT consecutive
+// positions each.  Called by select_stage_kernel (NT = 1024) and by the
+// verify call's second kernel next to the combine (NT = 256).
+template <bool AGG, int NT>
+__device__ __forceinline__ void stage_block(const SelArgs &a, const StageWs &o, int b, int w) {
+  constexpr int PPT = kChunk / NT;  // positions per thread
+  constexpr int BPT = kBins1 / NT;  // histogram bins per thread
+  constexpr int NW = NT / kWave;
+  static_assert(PPT % 2 == 0 && BPT % 4 == 0, "block size");
   __shared__ uint32_t hist[kBins1];  // the histogram, then the counting-sort cursors
   __shared__ u32x2 staged[kChunk];
-  __shared__ int wsum[kStageWaves];
-  const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
+  __shared__ int wsum[NW];
+  const int t = threadIdx.x;
   // loads first, before the length is known (positions below max_prefix are
   // inside every row, and max_prefix is even)
-  const int j0 = w * kChunk + 2 * t;
-  const bool in_row = j0 < a.max_prefix;
+  const int j0 = w * kChunk + PPT * t;
   const int P = sel_prefix(a, b);
-  f32x2 sc = {0.f, 0.f};
+  f32x2 sc[PPT / 2];
+#pragma unroll
+  for (int i = 0; i < PPT / 2; ++i) sc[i] = f32x2{0.f, 0.f};
   if (AGG) {
     const int nrow = a.src_rows * a.src_heads;
     const float *base = a.src + (size_t)b * nrow * a.max_prefix + j0;
-    constexpr int U = 8;
-    for (int r0 = 0; r0 < nrow; r0 += U) {
-      f32x2 v[U];
+    constexpr int UR = 8;  // rows per batch (rows are summed in order: the same sums at any NT)
+    for (int r0 = 0; r0 < nrow; r0 += UR) {
+      f32x2 v[UR][PPT / 2];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        v[u] = (in_row && r0 + u < nrow)
-                   ? __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(base + (size_t)(r0 + u) * a.max_prefix))
-                   : f32x2{0.f, 0.f};
+      for (int u = 0; u < UR; ++u)
 #pragma unroll
-      for (int u = 0; u < U; ++u) sc += v[u];
+        for (int i = 0; i < PPT / 2; ++i)
+          v[u][i] = (j0 + 2 * i < a.max_prefix && r0 + u < nrow)
+                        ? __builtin_nontemporal_load(
+                              reinterpret_cast<const f32x2 *>(base + (size_t)(r0 + u) * a.max_prefix + 2 * i))
+                        : f32x2{0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < UR; ++u)
+#pragma unroll
+        for (int i = 0; i < PPT / 2; ++i) sc[i] += v[u][i];
     }
-  } else if (in_row) {
-    sc = *reinterpret_cast<const f32x2 *>(a.scores + (size_t)b * a.max_prefix + j0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < PPT / 2; ++i)
+      if (j0 + 2 * i < a.max_prefix)
+        sc[i] = *reinterpret_cast<const f32x2 *>(a.scores + (size_t)b * a.max_prefix + j0 + 2 * i);
   }
   const int nch = (P + kChunk - 1) / kChunk;
   if (w >= nch) return;
-  const bool v0 = j0 < P, v1 = j0 + 1 < P;
-  const uint32_t key0 = score_key(sc[0]), key1 = score_key(sc[1]);
+  uint32_t key[PPT];
 #pragma unroll
-  for (int i = 0; i < kBins1 / kStageThreads; ++i) hist[t + i * kStageThreads] = 0u;
-  __syncthreads();
-  if (v0) atomicAdd(&hist[key0 >> 20], 1u);
-  if (v1) atomicAdd(&hist[key1 >> 20], 1u);
-  __syncthreads();
-  // cnt_ge: thread t owns bins [4096 - 4 (t + 1), 4096 - 4 t), highest first
-  const int top = kBins1 - 4 * t;
-  uint32_t hh[4], ge[4];
+  for (int i = 0; i < PPT; ++i) key[i] = score_key(sc[i / 2][i % 2]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) hh[i] = hist[top - 1 - i];
+  for (int i = 0; i < BPT; ++i) hist[t + i * NT] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PPT; ++i)
+    if (j0 + i < P) atomicAdd(&hist[key[i] >> 20], 1u);
+  __syncthreads();
+  // cnt_ge: thread t owns bins [4096 - BPT (t + 1), 4096 - BPT t), highest first
+  const int top = kBins1 - BPT * t;
+  uint32_t hh[BPT], ge[BPT];
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) hh[i] = hist[top - 1 - i];
   {
     int local = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) local += (int)hh[i];
+    for (int i = 0; i < BPT; ++i) local += (int)hh[i];
     int total;
-    int run = block_scan_n<kStageWaves>(local, wsum, total);
+    int run = block_scan_n<NW>(local, wsum, total);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < BPT; ++i) {
       run += (int)hh[i];
       ge[i] = (uint32_t)run;  // keys in bin top - 1 - i or above
     }
   }
   // counting sort by bin, highest first: the cursor starts at the keys above the bin
 #pragma unroll
-  for (int i = 0; i < 4; ++i) hist[top - 1 - i] = ge[i] - hh[i];
+  for (int i = 0; i < BPT; ++i) hist[top - 1 - i] = ge[i] - hh[i];
   __syncthreads();
-  if (v0) staged[atomicAdd(&hist[key0 >> 20], 1u)] = u32x2{key0, (uint32_t)j0};
-  if (v1) staged[atomicAdd(&hist[key1 >> 20], 1u)] = u32x2{key1, (uint32_t)(j0 + 1)};
+#pragma unroll
+  for (int i = 0; i < PPT; ++i)
+    if (j0 + i < P) staged[atomicAdd(&hist[key[i] >> 20], 1u)] = u32x2{key[i], (uint32_t)(j0 + i)};
   __syncthreads();
   // global writes, after the last barrier
   if (AGG) {
     float *dst = a.scores_out + (size_t)b * a.max_prefix + j0;
-    if (v1) *reinterpret_cast<f32x2 *>(dst) = sc;
-    else if (v0) dst[0] = sc[0];
+#pragma unroll
+    for (int i = 0; i < PPT / 2; ++i) {
+      if (j0 + 2 * i + 1 < P) *reinterpret_cast<f32x2 *>(dst + 2 * i) = sc[i];
+      else if (j0 + 2 * i < P) dst[2 * i] = sc[i][0];
+    }
   }
   uint16_t *row = o.cnt_ge + ((size_t)b * o.chunks + w) * kCntStride;
-  *reinterpret_cast<u32x2 *>(row + top - 4) = u32x2{ge[3] | (ge[2] << 16), ge[1] | (ge[0] << 16)};
+#pragma unroll
+  for (int i = 0; i < BPT; i += 4)  // bins top - 4 - i .. top - 1 - i, lowest first
+    *reinterpret_cast<u32x2 *>(row + top - 4 - i) =
+        u32x2{ge[i + 3] | (ge[i + 2] << 16), ge[i + 1] | (ge[i] << 16)};
   if (t == 0) row[kBins1] = 0;
-  if ((t & 15) == 15) {  // bin 64 j is the lowest of thread 1023 - 16 j's four bins
-    const int j = (kStageThreads - 1 - t) >> 4;
-    o.coarse[((size_t)b * 64 + j) * kSplitMaxChunks + w] = (uint16_t)ge[3];
+  constexpr int TPC = 64 / BPT;  // threads per 64 bins
+  if (t % TPC == TPC - 1) {      // bin 64 j is the lowest of thread NT - 1 - TPC j's bins
+    const int j = (NT - 1 - t) / TPC;
+    o.coarse[((size_t)b * 64 + j) * kSplitMaxChunks + w] = (uint16_t)ge[BPT - 1];
   }
   const int n = min(P - w * kChunk, kChunk);
   u32x2 *dst = a.ws.cand + (size_t)b * a.max_prefix + (size_t)w * kChunk;
-  if (2 * t + 1 < n)
-    *reinterpret_cast<u32x4 *>(dst + 2 * t) =
-        u32x4{staged[2 * t][0], staged[2 * t][1], staged[2 * t + 1][0], staged[2 * t + 1][1]};
-  else if (2 * t < n)
-    dst[2 * t] = staged[2 * t];
+#pragma unroll
+  for (int i = 0; i < PPT; i += 2) {
+    const int e = PPT * t + i;
+    if (e + 1 < n)
+      *reinterpret_cast<u32x4 *>(dst + e) = u32x4{staged[e][0], staged[e][1], staged[e + 1][0], staged[e + 1][1]};
+    else if (e < n)
+      dst[e] = staged[e];
+  }
+}
+
+template <bool AGG>
+__global__ __launch_bounds__(kStageThreads, 2) void select_stage_kernel(SelArgs a, StageWs o) {
+  stage_block<AGG, kStageThreads>(a, o, blockIdx.y, blockIdx.x);
 }
 
 // ---------------------------------------------------------------- resolve

@@ -132,10 +132,21 @@ void launch_combine(int rpb, const AttnArgs &a, dim3 grid, hipStream_t st) {
   }
 }
 
-// Attention kernel over the shared key lists, then combine blocks of one or
-// more rows per (KV head, sequence).
+// Rows per combine block: as many as leave each row enough partial groups
+// to load its (at most) np partials in one batch of 8 per thread.
+int combine_rows_per_block(const vg_shape *s, const AttnPlan &p) {
+  const int cols = s->head_dim / 4;
+  const long long bg = (long long)s->batch * s->num_kv_heads;
+  const long long np = p.split_tokens > 0 ? p.splits : (p.workgroups + bg - 1) / bg + 1;
+  int rpb = 1;
+  while (rpb < 8 && (kThreads / (2 * rpb)) / cols * 8 >= np && kThreads / (2 * rpb) >= cols) rpb *= 2;
+  return rpb;
+}
+
+// Attention kernel over the shared key lists, then (with_combine) combine
+// blocks of one or more rows per (KV head, sequence).
 vg_status launch_attention(const vg_shape *s, const AttnPlan &p, AttnArgs &a, char *ws,
-                           hipStream_t st) {
+                           hipStream_t st, bool with_combine = true) {
   a.part_o = reinterpret_cast<float *>(ws + p.off_part_o);
   a.part_ml = reinterpret_cast<float *>(ws + p.off_part_ml);
   a.batch = s->batch;
@@ -163,13 +174,8 @@ vg_status launch_attention(const vg_shape *s, const AttnPlan &p, AttnArgs &a, ch
       else launch_valu_f3264(p.mr, a, grid, st);
     }
   }
-  // Rows per combine block: as many as leave each row enough partial groups
-  // to load its (at most) np partials in one batch of 8 per thread.
-  const int cols = s->head_dim / 4;
-  const long long bg = (long long)s->batch * s->num_kv_heads;
-  const long long np = p.split_tokens > 0 ? p.splits : (p.workgroups + bg - 1) / bg + 1;
-  int rpb = 1;
-  while (rpb < 8 && (kThreads / (2 * rpb)) / cols * 8 >= np && kThreads / (2 * rpb) >= cols) rpb *= 2;
+  if (!with_combine) return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
+  const int rpb = combine_rows_per_block(s, p);
   const dim3 cgrid((p.rows + rpb - 1) / rpb, s->num_kv_heads, s->batch);
   if (s->head_dim == 128) launch_combine<128>(rpb, a, cgrid, st);
   else launch_combine<64>(rpb, a, cgrid, st);
@@ -228,14 +234,16 @@ SelWs sel_ws(const SelPlan &p, void *ws) {
 
 constexpr int kMaxSelectPrefix = kMaxChunks * kChunk;
 
-vg_status verify_impl(const vg_shape *shape, const void *q, const void *k_cache, const void *v_cache,
-                      const int32_t *page_table, const int32_t *prefix_len, int32_t max_prefix,
-                      int32_t gamma, float *out, float *logits, float *group_scores, void *workspace,
-                      size_t workspace_bytes, void *stream, bool export_all) {
+// Validation and launch arguments of a verify call (vg_verify_attention and
+// the calls built on it).
+vg_status verify_prepare(const vg_shape *shape, const void *q, const void *k_cache, const void *v_cache,
+                         const int32_t *page_table, const int32_t *prefix_len, int32_t max_prefix,
+                         int32_t gamma, float *out, float *logits, float *group_scores, void *workspace,
+                         size_t workspace_bytes, bool export_all, AttnPlan &p, AttnArgs &a) {
   if (!valid_shape(shape) || max_prefix < 0 || gamma < 0 || gamma > 15) return VG_ERR_INVALID_ARG;
   const void *req[] = {q, k_cache, v_cache, page_table, prefix_len, out};
-  for (const void *p : req)
-    if (!p || !aligned16(p)) return VG_ERR_INVALID_ARG;
+  for (const void *ptr : req)
+    if (!ptr || !aligned16(ptr)) return VG_ERR_INVALID_ARG;
   if ((logits && !aligned16(logits)) || (group_scores && !aligned16(group_scores)))
     return VG_ERR_INVALID_ARG;
   const vg_status sup = supported_shape(shape);
@@ -245,10 +253,10 @@ vg_status verify_impl(const vg_shape *shape, const void *q, const void *k_cache,
   if (R * G > kMaxRows) return VG_ERR_UNSUPPORTED;
   if (ceil_div((long long)max_prefix + R, shape->page_size) > shape->max_pages_per_seq)
     return VG_ERR_INVALID_ARG;
-  const AttnPlan p = plan_attention(shape, R, (long long)max_prefix + R, false);
+  p = plan_attention(shape, R, (long long)max_prefix + R, false);
   if (!p.ok) return VG_ERR_UNSUPPORTED;
   if (!workspace || !aligned16(workspace) || workspace_bytes < p.bytes) return VG_ERR_WORKSPACE;
-  AttnArgs a{};
+  a = AttnArgs{};
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
@@ -268,8 +276,48 @@ vg_status verify_impl(const vg_shape *shape, const void *q, const void *k_cache,
   a.scale_log2 = a.scale * kLog2e;
   a.sparse = 0;
   a.export_all = export_all ? 1 : 0;
-  return launch_attention(shape, p, a, static_cast<char *>(workspace),
-                          static_cast<hipStream_t>(stream));
+  return VG_OK;
+}
+
+vg_status verify_impl(const vg_shape *shape, const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *page_table, const int32_t *prefix_len, int32_t max_prefix,
+                      int32_t gamma, float *out, float *logits, float *group_scores, void *workspace,
+                      size_t workspace_bytes, void *stream, bool export_all) {
+  AttnPlan p;
+  AttnArgs a;
+  const vg_status st = verify_prepare(shape, q, k_cache, v_cache, page_table, prefix_len, max_prefix, gamma, out,
+                                      logits, group_scores, workspace, workspace_bytes, export_all, p, a);
+  if (st != VG_OK) return st;
+  return launch_attention(shape, p, a, static_cast<char *>(workspace), static_cast<hipStream_t>(stream));
+}
+
+// The verify call's second kernel with the selection's first step beside it:
+// blocks [0, nstage) stage one chunk of the group export each (stage_block),
+// the others are the verify combine's blocks (grid (ncomb_x, Hkv, B),
+// flattened).  The export is complete when this kernel starts: the attention
+// kernel before it wrote it.
+template <int D, int RPB>
+__global__ __launch_bounds__(kThreads) void combine_stage_kernel(AttnArgs a, SelArgs s, StageWs o, int ncomb_x,
+                                                                int nstage_x) {
+  const int id = blockIdx.x, nstage = nstage_x * s.batch;
+  if (id < nstage) {
+    stage_block<true, kThreads>(s, o, id / nstage_x, id % nstage_x);
+    return;
+  }
+  const int c = id - nstage, Hkv = a.num_kv_heads;
+  combine_block<D, RPB>(a, c % ncomb_x, (c / ncomb_x) % Hkv, c / (ncomb_x * Hkv));
+}
+
+template <int D>
+void launch_combine_stage(int rpb, const AttnArgs &a, const SelArgs &s, const StageWs &o, int ncomb_x,
+                          int nstage_x, hipStream_t st) {
+  const dim3 grid(nstage_x * s.batch + ncomb_x * a.num_kv_heads * a.batch);
+  switch (rpb) {
+    case 1: hipLaunchKernelGGL((combine_stage_kernel<D, 1>), grid, dim3(kThreads), 0, st, a, s, o, ncomb_x, nstage_x); break;
+    case 2: hipLaunchKernelGGL((combine_stage_kernel<D, 2>), grid, dim3(kThreads), 0, st, a, s, o, ncomb_x, nstage_x); break;
+    case 4: hipLaunchKernelGGL((combine_stage_kernel<D, 4>), grid, dim3(kThreads), 0, st, a, s, o, ncomb_x, nstage_x); break;
+    default: hipLaunchKernelGGL((combine_stage_kernel<D, 8>), grid, dim3(kThreads), 0, st, a, s, o, ncomb_x, nstage_x); break;
+  }
 }
 
 // ---------------------------------------------------------------- scratch
@@ -530,6 +578,66 @@ vg_status vg_aggregate_topk_select(int32_t batch, const float *src, int32_t src_
     hipLaunchKernelGGL(select_pass2_kernel, grid, dim3(kSelThreads), 0, st, a);
     hipLaunchKernelGGL(select_pass3_kernel, grid, dim3(kSelThreads), 0, st, a);
   }
+  return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
+}
+
+vg_status vg_verify_select(const vg_shape *shape, const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *page_table, const int32_t *prefix_len, int32_t max_prefix, int32_t gamma,
+                           float *out, float *group_scores, float *scores, const int32_t *k, int32_t max_k,
+                           int32_t *sel_pos, int32_t *sel_slot, int32_t *sel_count, void *verify_ws,
+                           size_t verify_ws_bytes, void *select_ws, size_t select_ws_bytes, void *stream) {
+  if (!group_scores) return VG_ERR_INVALID_ARG;
+  AttnPlan p;
+  AttnArgs a;
+  const vg_status vst = verify_prepare(shape, q, k_cache, v_cache, page_table, prefix_len, max_prefix, gamma, out,
+                                       nullptr, group_scores, verify_ws, verify_ws_bytes, false, p, a);
+  if (vst != VG_OK) return vst;
+  if (max_k < 0) return VG_ERR_INVALID_ARG;
+  const void *req[] = {scores, k, sel_pos, sel_count};
+  for (const void *ptr : req)
+    if (!ptr || !aligned16(ptr)) return VG_ERR_INVALID_ARG;
+  if (sel_slot && !aligned16(sel_slot)) return VG_ERR_INVALID_ARG;
+  if (max_prefix > kMaxSelectPrefix) return VG_ERR_UNSUPPORTED;
+  const int B = shape->batch, Hkv = shape->num_kv_heads;
+  const SelPlan sp = plan_select(B, max_prefix);
+  if (!select_ws || !aligned16(select_ws) || select_ws_bytes < sp.bytes) return VG_ERR_WORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (!split_ok(B, max_prefix, sel_slot != nullptr, shape->page_size)) {
+    // the same work as the separate calls
+    const vg_status st = launch_attention(shape, p, a, static_cast<char *>(verify_ws), hs);
+    if (st != VG_OK) return st;
+    return vg_aggregate_topk_select(B, group_scores, 1, Hkv, prefix_len, max_prefix, scores, k, max_k, page_table,
+                                    shape->page_size, shape->max_pages_per_seq, sel_pos, sel_slot, sel_count,
+                                    select_ws, select_ws_bytes, stream);
+  }
+  SelArgs sa{};
+  sa.batch = B;
+  sa.max_prefix = max_prefix;
+  sa.max_k = max_k;
+  sa.prefix_len = prefix_len;
+  sa.k = k;
+  sa.scores = scores;
+  sa.scores_out = scores;
+  sa.src = group_scores;
+  sa.src_rows = 1;
+  sa.src_heads = Hkv;
+  sa.page_table = page_table;
+  sa.page_size = shape->page_size;
+  sa.max_pages = shape->max_pages_per_seq;
+  sa.sel_pos = sel_pos;
+  sa.sel_slot = sel_slot;
+  sa.sel_count = sel_count;
+  sa.ws = sel_ws(sp, select_ws);
+  const StageWs o = stage_ws(sp, select_ws);
+  // attention kernel; then combine and the selection's staging in one launch;
+  // then the selection's resolve
+  const vg_status st = launch_attention(shape, p, a, static_cast<char *>(verify_ws), hs, false);
+  if (st != VG_OK) return st;
+  const int rpb = combine_rows_per_block(shape, p);
+  const int ncomb_x = (p.rows + rpb - 1) / rpb;
+  if (shape->head_dim == 128) launch_combine_stage<128>(rpb, a, sa, o, ncomb_x, sp.chunks, hs);
+  else launch_combine_stage<64>(rpb, a, sa, o, ncomb_x, sp.chunks, hs);
+  hipLaunchKernelGGL(select_resolve_kernel, dim3(sp.chunks, B), dim3(kResolveThreads), 0, hs, sa, o);
   return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
 }
 

@@ -131,6 +131,13 @@ class DeviceCase:
                                     self.sel_pos, self.sel_slot, self.sel_count, self.ws_select,
                                     self.ws_select_bytes, stream)
 
+    def verify_select(self, stream=None):
+        """Verify with the group export, aggregation and top-k in one call (vg_verify_select)."""
+        vg.vg_verify_select(self.shape, self.q, self.k_cache, self.v_cache, self.page_table, self.prefix_len,
+                            self.max_prefix, self.gamma, self.out, self.group, self.scores, self.k, self.max_k,
+                            self.sel_pos, self.sel_slot, self.sel_count, self.ws_verify, self.ws_verify_bytes,
+                            self.ws_select, self.ws_select_bytes, stream)
+
     def window(self, n_sink=4, stream=None):
         """Query-agnostic selection into the same buffers as topk(): n_sink sink
         positions plus the most recent ones, k_b in all."""
@@ -177,9 +184,11 @@ class DeviceCase:
 
     def iteration(self, export="group", rows="two", stream=None):
         """One pass of the whole path: verify (+export), aggregate, top-k, gamma draft steps."""
-        self.verify(export=export, rows=rows, stream=stream)
-        src = "group" if export == "group" else ("raw" if rows == "two" else "raw_all")
-        self.select(src=src, stream=stream)
+        if export == "group" and rows == "two":
+            self.verify_select(stream=stream)
+        else:
+            self.verify(export=export, rows=rows, stream=stream)
+            self.select(src="raw" if rows == "two" else "raw_all", stream=stream)
         for s in range(self.gamma):
             self.sparse(step=s, stream=stream)
 
