@@ -49,6 +49,7 @@ constexpr int kSplitMaxChunks = kSplitMaxPrefix / kChunk;  // 64: one wave takes
 constexpr int kCntStride = kBins1 + 8;                     // u16 per chunk row of cnt_ge (16-byte rows)
 constexpr int kResolveCache = 6144;                        // candidates kept in LDS
 constexpr int kCandPiece = kWave;                          // candidates per read item
+constexpr int kItemBatch = 12;                             // candidate items per wave per batch of loads
 
 // Workspace pieces of the two-launch selection (besides SelWs.cand, which
 // holds the staged pairs: chunk c at offset c * kChunk).
@@ -121,7 +122,9 @@ __device__ __forceinline__ int find_bin_n(const uint32_t (&h)[PER], int nbins, i
 // ---------------------------------------------------------------- stage
 // One chunk (w) of sequence b by a block of NT threads, 2048 / NT consecutive
 // positions each.  Called by select_stage_kernel (NT = 1024) and by the
-// verify call's second kernel next to the combine (NT = 256).
+// verify call's second kernel next to the combine (NT = 256).  Thread t holds
+// the position pairs t, t + NT, t + 2 NT, ... of the chunk, so that each load
+// instruction of a wave reads 512 contiguous bytes of an export row.
 template <bool AGG, int NT>
 __device__ __forceinline__ void stage_block(const SelArgs &a, const StageWs &o, int b, int w) {
   constexpr int PPT = kChunk / NT;  // positions per thread
@@ -134,14 +137,15 @@ __device__ __forceinline__ void stage_block(const SelArgs &a, const StageWs &o, 
   const int t = threadIdx.x;
   // loads first, before the length is known (positions below max_prefix are
   // inside every row, and max_prefix is even)
-  const int j0 = w * kChunk + PPT * t;
+  const int c0 = w * kChunk;
+  auto pos_of = [&](int i) { return c0 + 2 * (t + NT * (i / 2)) + (i & 1); };  // position of key i
   const int P = sel_prefix(a, b);
   f32x2 sc[PPT / 2];
 #pragma unroll
   for (int i = 0; i < PPT / 2; ++i) sc[i] = f32x2{0.f, 0.f};
   if (AGG) {
     const int nrow = a.src_rows * a.src_heads;
-    const float *base = a.src + (size_t)b * nrow * a.max_prefix + j0;
+    const float *base = a.src + (size_t)b * nrow * a.max_prefix;
     constexpr int UR = 8;  // rows per batch (rows are summed in order: the same sums at any NT)
     for (int r0 = 0; r0 < nrow; r0 += UR) {
       f32x2 v[UR][PPT / 2];
@@ -149,9 +153,9 @@ __device__ __forceinline__ void stage_block(const SelArgs &a, const StageWs &o, 
       for (int u = 0; u < UR; ++u)
 #pragma unroll
         for (int i = 0; i < PPT / 2; ++i)
-          v[u][i] = (j0 + 2 * i < a.max_prefix && r0 + u < nrow)
-                        ? __builtin_nontemporal_load(
-                              reinterpret_cast<const f32x2 *>(base + (size_t)(r0 + u) * a.max_prefix + 2 * i))
+          v[u][i] = (pos_of(2 * i) < a.max_prefix && r0 + u < nrow)
+                        ? __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(
+                              base + (size_t)(r0 + u) * a.max_prefix + pos_of(2 * i)))
                         : f32x2{0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < UR; ++u)
@@ -161,8 +165,8 @@ __device__ __forceinline__ void stage_block(const SelArgs &a, const StageWs &o, 
   } else {
 #pragma unroll
     for (int i = 0; i < PPT / 2; ++i)
-      if (j0 + 2 * i < a.max_prefix)
-        sc[i] = *reinterpret_cast<const f32x2 *>(a.scores + (size_t)b * a.max_prefix + j0 + 2 * i);
+      if (pos_of(2 * i) < a.max_prefix)
+        sc[i] = *reinterpret_cast<const f32x2 *>(a.scores + (size_t)b * a.max_prefix + pos_of(2 * i));
   }
   const int nch = (P + kChunk - 1) / kChunk;
   if (w >= nch) return;
@@ -174,7 +178,7 @@ __device__ __forceinline__ void stage_block(const SelArgs &a, const StageWs &o, 
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < PPT; ++i)
-    if (j0 + i < P) atomicAdd(&hist[key[i] >> 20], 1u);
+    if (pos_of(i) < P) atomicAdd(&hist[key[i] >> 20], 1u);
   __syncthreads();
   // cnt_ge: thread t owns bins [4096 - BPT (t + 1), 4096 - BPT t), highest first
   const int top = kBins1 - BPT * t;
@@ -199,15 +203,16 @@ __device__ __forceinline__ void stage_block(const SelArgs &a, const StageWs &o, 
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < PPT; ++i)
-    if (j0 + i < P) staged[atomicAdd(&hist[key[i] >> 20], 1u)] = u32x2{key[i], (uint32_t)(j0 + i)};
+    if (pos_of(i) < P) staged[atomicAdd(&hist[key[i] >> 20], 1u)] = u32x2{key[i], (uint32_t)pos_of(i)};
   __syncthreads();
   // global writes, after the last barrier
   if (AGG) {
-    float *dst = a.scores_out + (size_t)b * a.max_prefix + j0;
+    float *dst = a.scores_out + (size_t)b * a.max_prefix;
 #pragma unroll
     for (int i = 0; i < PPT / 2; ++i) {
-      if (j0 + 2 * i + 1 < P) *reinterpret_cast<f32x2 *>(dst + 2 * i) = sc[i];
-      else if (j0 + 2 * i < P) dst[2 * i] = sc[i][0];
+      const int p = pos_of(2 * i);
+      if (p + 1 < P) *reinterpret_cast<f32x2 *>(dst + p) = sc[i];
+      else if (p < P) dst[p] = sc[i][0];
     }
   }
   uint16_t *row = o.cnt_ge + ((size_t)b * o.chunks + w) * kCntStride;
@@ -242,7 +247,6 @@ __global__ __launch_bounds__(kStageThreads, 2) void select_stage_kernel(SelArgs 
 struct ResolveSmem {
   u32x2 cache[kResolveCache];  // the sequence's candidates, chunk by chunk
   uint32_t h[kBins23];
-  int items[kSplitMaxChunks * (kChunk / kCandPiece)];  // candidate reads: chunk << 8 | piece
   int32_t out[kChunk];         // this chunk's selected positions, ascending
   int part[kResolveWaves][kWave];
   int part64[kResolveWaves];
@@ -253,6 +257,7 @@ struct ResolveSmem {
   uint32_t bm[kChunk / 32];   // this chunk's selected positions
   uint32_t tie[kChunk / 32];  // this chunk's keys equal to K*
   int32_t page[kChunk / kPageSize];
+  u32x2 list[kWave];  // the candidates of the second-level bin holding K*, when few
   int meta[8];
 };
 
@@ -261,7 +266,22 @@ __global__ __launch_bounds__(kResolveThreads, 2) void select_resolve_kernel(SelA
   __shared__ int wsum[kResolveWaves];
   __shared__ int res[4][4];
   const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const bool want_slots = a.sel_slot != nullptr;
+  // ---- round 1: G(64 j) = the sum over chunks of cnt_ge[c][64 j] (lane =
+  // chunk, wave v takes j = v + 8 m), and this chunk's page ids.  The loads
+  // are issued before the length and k are known (every column of the coarse
+  // table is inside the workspace; columns past the sequence's chunks are
+  // masked).
+  uint32_t g1[8];
+  {
+    const uint16_t *crow = o.coarse + (size_t)b * 64 * kSplitMaxChunks + lane;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) g1[m] = crow[(wave + kResolveWaves * m) * kSplitMaxChunks];
+  }
+  int pid = 0;
+  if (want_slots && t < kChunk / kPageSize)
+    pid = a.page_table[(size_t)b * a.max_pages + min(w * (kChunk / kPageSize) + t, a.max_pages - 1)];
   const int P = sel_prefix(a, b);
   const int kk = sel_k(a, b, P);
   const int nch = (P + kChunk - 1) / kChunk;
@@ -270,22 +290,10 @@ __global__ __launch_bounds__(kResolveThreads, 2) void select_resolve_kernel(SelA
     if (w == 0 && t == 0) a.sel_count[b] = 0;
     return;
   }
-  const bool want_slots = a.sel_slot != nullptr;
-  const int c_ln = min(lane, nch - 1);
   const bool live_ln = lane < nch;
-  // ---- round 1: G(64 j) = the sum over chunks of cnt_ge[c][64 j] (lane =
-  // chunk, wave v takes j = v + 8 m), and this chunk's page ids
   {
-    const uint16_t *crow = o.coarse + (size_t)b * 64 * kSplitMaxChunks + c_ln;
-    uint32_t g1[8];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const uint32_t x = crow[(wave + kResolveWaves * m) * kSplitMaxChunks];
-      g1[m] = live_ln ? x : 0u;
-    }
-    int pid = 0;
-    if (want_slots && t < kChunk / kPageSize)
-      pid = a.page_table[(size_t)b * a.max_pages + min(w * (kChunk / kPageSize) + t, a.max_pages - 1)];
+    for (int m = 0; m < 8; ++m) g1[m] = live_ln ? g1[m] : 0u;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int sum = __builtin_amdgcn_readlane(wave_inclusive_scan((int)g1[m]), 63);
@@ -300,6 +308,7 @@ __global__ __launch_bounds__(kResolveThreads, 2) void select_resolve_kernel(SelA
       S.gt[t] = 0;
       S.eq[t] = 0;
     }
+    if (t == 0) S.meta[5] = 0;
     S.h[t] = 0u;
     S.h[t + kResolveThreads] = 0u;
   }
@@ -330,24 +339,20 @@ __global__ __launch_bounds__(kResolveThreads, 2) void select_resolve_kernel(SelA
     if (lane == 0) S.part64[wave] = s64;
   }
   __syncthreads();  // (also: every wave has read the first round's sums)
-  if (wave == 0) {
+  // every wave: G at the window's bins (lane = bin), the bin b1 holding K*
+  // and the keys above it
+  int jb, k1;
+  {
     int g2 = 0, g64 = 0;
 #pragma unroll
     for (int q = 0; q < kResolveWaves; ++q) {
       g2 += S.part[q][lane];
       g64 += S.part64[q];
     }
-    const int jb = 63 - (int)__builtin_clzll(__builtin_amdgcn_ballot_w64(g2 >= kk));  // G(base2) >= kk
-    const int above = jb < 63 ? __shfl(g2, jb + 1) : g64;
-    if (lane == 0) {
-      S.meta[0] = jb;
-      S.meta[1] = above;
-    }
+    jb = 63 - (int)__builtin_clzll(__builtin_amdgcn_ballot_w64(g2 >= kk));  // G(base2) >= kk
+    k1 = kk - (jb < 63 ? __shfl(g2, jb + 1) : g64);  // rank of K* inside bin b1 (>= 1)
   }
-  __syncthreads();
-  const int jb = S.meta[0];
   const uint32_t b1 = (uint32_t)(base2 + jb);
-  const int k1 = kk - S.meta[1];  // rank of K* inside bin b1 (>= 1)
   // each chunk's counts at b1 and b1 + 1, from the loading lanes' registers
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
@@ -359,55 +364,61 @@ __global__ __launch_bounds__(kResolveThreads, 2) void select_resolve_kernel(SelA
     }
   }
   __syncthreads();
-  // wave 0: candidates before each chunk, and the candidate read items
+  // every wave: per chunk (lane = chunk) its candidates (the entries of bin
+  // b1), their offset in the sequence's candidate list, and the 64-entry read
+  // items of its candidates
+  const int lo_ln = live_ln ? S.lo[lane] : 0;
+  const int nc_ln = live_ln ? S.hi[lane] - lo_ln : 0;
+  const int cd = wave_inclusive_scan(nc_ln);
+  const int off_ln = cd - nc_ln;
+  const int n_cand = __builtin_amdgcn_readlane(cd, 63);
+  const int np_ln = (nc_ln + kCandPiece - 1) / kCandPiece;
+  const int io_ln = wave_inclusive_scan(np_ln);  // items of chunks 0 .. lane
+  const int n_items = __builtin_amdgcn_readlane(io_ln, 63);
   if (wave == 0) {
-    const int nc = live_ln ? S.hi[lane] - S.lo[lane] : 0;
-    const int cd = wave_inclusive_scan(nc);
-    if (live_ln) S.cand_off[lane] = cd - nc;
-    if (lane == 63) S.cand_off[nch] = cd;
-    const int np = (nc + kCandPiece - 1) / kCandPiece;
-    const int io = wave_inclusive_scan(np);
-    for (int r = 0; r < np; ++r) S.items[io - np + r] = (lane << 8) | r;
-    if (lane == 63) S.meta[2] = io;
+    if (live_ln) S.cand_off[lane] = off_ln;
+    if (lane == 63) S.cand_off[nch] = n_cand;
   }
-  __syncthreads();
-  const int n_cand = S.cand_off[nch];
   const bool cached = n_cand <= kResolveCache;
   const u32x2 *stg = a.ws.cand + (size_t)b * a.max_prefix;
-  // ---- round 3: this chunk's entries above b1 (their bits), and every
-  // candidate into the LDS cache (wave v takes items v, v + 8, ...)
+  // ---- round 3: this chunk's entries above b1 (their positions), and every
+  // candidate into the LDS cache (wave v takes items v, v + 8, ...,
+  // kItemBatch of them per batch; an item's chunk and offsets are
+  // wave-uniform).  The first own load and the first batch of items are in
+  // flight together; more of either is rare.
   {
-    const int lo_own = S.lo[w];
-    const int n_items = cached ? S.meta[2] : 0;
-    constexpr int Q = 4;
-    for (int r0 = 0;; r0 += Q) {
-      const int it_base = wave + kResolveWaves * r0;
-      const int own_base = kResolveThreads * r0;
-      if (it_base >= n_items && own_base >= lo_own) break;  // (wave-uniform for items; own work is per thread)
-      u32x2 v[Q], u[Q];
-      int c_of[Q], i_of[Q];
+    const int lo_own = __builtin_amdgcn_readlane(lo_ln, w);
+    const uint32_t *own_pos = reinterpret_cast<const uint32_t *>(stg + (size_t)w * kChunk) + 1;
+    auto mark_own = [&](int e, uint32_t pos) {
+      if (e < lo_own) {
+        const int p = (int)pos - w * kChunk;
+        atomicOr(&S.bm[p >> 5], 1u << (p & 31));
+      }
+    };
+    const uint32_t up0 = own_pos[2 * min(t, max(lo_own - 1, 0))];
+    const int n_it = cached ? n_items : 0;
+    auto item_batch = [&](int r0) {
+      u32x2 v[kItemBatch];
+      int dst[kItemBatch];
 #pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        const int it = it_base + kResolveWaves * q;
-        const int item = S.items[min(it, max(n_items - 1, 0))];
-        const int c = item >> 8, i = kCandPiece * (item & 255) + lane;
-        const bool ok = it < n_items && i < S.hi[c] - S.lo[c];
-        c_of[q] = ok ? c : -1;
-        i_of[q] = i;
-        v[q] = stg[ok ? (size_t)c * kChunk + S.lo[c] + i : 0];
-        const int e = own_base + kResolveThreads * q + t;
-        u[q] = stg[(size_t)w * kChunk + min(e, max(lo_own - 1, 0))];
+      for (int q = 0; q < kItemBatch; ++q) {
+        const int it = r0 + kResolveWaves * q;
+        // the first chunk whose items reach past `it` (chunk 63 if none: then !ok)
+        const int c = __builtin_amdgcn_readfirstlane(
+            (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(io_ln > it) | (1ull << 63)));
+        const int i = kCandPiece * (it - __builtin_amdgcn_readlane(io_ln - np_ln, c)) + lane;
+        const bool ok = it < n_it && i < __builtin_amdgcn_readlane(nc_ln, c);
+        dst[q] = ok ? __builtin_amdgcn_readlane(off_ln, c) + i : -1;
+        v[q] = stg[ok ? (size_t)c * kChunk + __builtin_amdgcn_readlane(lo_ln, c) + i : 0];
       }
 #pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        if (c_of[q] >= 0) S.cache[S.cand_off[c_of[q]] + i_of[q]] = v[q];
-        const int e = own_base + kResolveThreads * q + t;
-        if (e < lo_own) {
-          const int p = (int)u[q][1] - w * kChunk;
-          atomicOr(&S.bm[p >> 5], 1u << (p & 31));
-        }
-      }
-    }
+      for (int q = 0; q < kItemBatch; ++q)
+        if (dst[q] >= 0) S.cache[dst[q]] = v[q];
+    };
+    if (wave < n_it) item_batch(wave);
+    mark_own(t, up0);
+    for (int r0 = wave + kResolveWaves * kItemBatch; r0 < n_it; r0 += kResolveWaves * kItemBatch) item_batch(r0);
+    for (int e = t + kResolveThreads; e < lo_own; e += kResolveThreads) mark_own(e, own_pos[2 * e]);
   }
   __syncthreads();
   // candidate i (0 <= i < n_cand) of the sequence
@@ -423,47 +434,92 @@ __global__ __launch_bounds__(kResolveThreads, 2) void select_resolve_kernel(SelA
   uint32_t hb[2] = {S.h[kBins23 - 1 - 2 * t], S.h[kBins23 - 2 - 2 * t]};
   int above2, n_b2;
   const uint32_t b2 = (uint32_t)find_bin_n<kResolveWaves, 2>(hb, kBins23, k1, wsum, res[0], above2, n_b2);
-  const int k2 = k1 - above2;
+  const int k2 = k1 - above2;  // rank of K* inside bin b2 (>= 1)
   const uint32_t pre22 = (b1 << 10) | b2;
-  S.h[kBins23 - 1 - 2 * t] = 0u;  // each thread clears the bins it read
-  S.h[kBins23 - 2 - 2 * t] = 0u;
-  __syncthreads();
-  for (int i = t; i < n_cand; i += kResolveThreads) {
-    const uint32_t key = cand(i)[0];
-    if ((key >> 10) == pre22) atomicAdd(&S.h[key & 1023u], 1u);
-  }
-  __syncthreads();
-  hb[0] = S.h[kBins23 - 1 - 2 * t];
-  hb[1] = S.h[kBins23 - 2 - 2 * t];
-  int above3, n_eq;
-  const uint32_t b3 = (uint32_t)find_bin_n<kResolveWaves, 2>(hb, kBins23, k2, wsum, res[1], above3, n_eq);
-  const uint32_t kstar = (pre22 << 10) | b3;
-  const int ties = k2 - above3;  // keys equal to K* to keep, lowest positions first
-  // ---- per chunk: candidates above and equal to K* (a candidate's chunk is
-  // its position / 2048); this chunk's own go to its bitmaps
-  for (int i = t; i < n_cand; i += kResolveThreads) {
-    const u32x2 e = cand(i);
-    const int c = (int)(e[1] >> 11);
-    if (e[0] > kstar) {
-      atomicAdd(&S.gt[c], 1);
-      if (c == w) atomicOr(&S.bm[(e[1] & (kChunk - 1)) >> 5], 1u << (e[1] & 31));
-    } else if (e[0] == kstar) {
-      atomicAdd(&S.eq[c], 1);
-      if (c == w) atomicOr(&S.tie[(e[1] & (kChunk - 1)) >> 5], 1u << (e[1] & 31));
+  int ties = 0;                 // keys equal to K* to keep, lowest positions first (wave 0)
+  int x_gt = 0, x_eq = 0;       // wave 0: chunk `lane`'s keys above / equal to K* from the list
+  uint32_t x_bm = 0u, x_tie = 0u;  // wave 0: bits of this chunk's bitmap word `lane` from the list
+  if (n_b2 <= kWave) {
+    // Few keys share K*'s top 22 bits: one pass over the candidates counts
+    // the keys above that bin per chunk (and marks this chunk's) and lists
+    // the bin's keys; wave 0 ranks the list.
+    for (int i = t; i < n_cand; i += kResolveThreads) {
+      const u32x2 e = cand(i);
+      const uint32_t h22 = e[0] >> 10;
+      if (h22 > pre22) {
+        const int c = (int)(e[1] >> 11);
+        atomicAdd(&S.gt[c], 1);
+        if (c == w) atomicOr(&S.bm[(e[1] & (kChunk - 1)) >> 5], 1u << (e[1] & 31));
+      } else if (h22 == pre22) {
+        S.list[atomicAdd(&S.meta[5], 1)] = e;
+      }
     }
+    __syncthreads();
+    if (wave == 0) {
+      const u32x2 mine = S.list[min(lane, n_b2 - 1)];
+      int gt_j = 0, ge_j = 0;  // list keys above / at least this lane's
+      for (int l = 0; l < n_b2; ++l) {
+        const uint32_t kl = S.list[l][0];
+        gt_j += kl > mine[0];
+        ge_j += kl >= mine[0];
+      }
+      // K* is the key of every lane with gt_j < k2 <= ge_j
+      const int src = __ffsll((unsigned long long)__builtin_amdgcn_ballot_w64(lane < n_b2 && gt_j < k2 && k2 <= ge_j)) - 1;
+      const uint32_t kstar = (uint32_t)__shfl((int)mine[0], src);
+      ties = k2 - __shfl(gt_j, src);
+      for (int l = 0; l < n_b2; ++l) {
+        const u32x2 e = S.list[l];
+        const int c = (int)(e[1] >> 11);
+        const bool gt = e[0] > kstar, eq = e[0] == kstar;
+        x_gt += (gt && c == lane);
+        x_eq += (eq && c == lane);
+        if (c == w && (int)((e[1] & (kChunk - 1)) >> 5) == lane) {
+          if (gt) x_bm |= 1u << (e[1] & 31);
+          if (eq) x_tie |= 1u << (e[1] & 31);
+        }
+      }
+    }
+  } else {
+    S.h[kBins23 - 1 - 2 * t] = 0u;  // each thread clears the bins it read
+    S.h[kBins23 - 2 - 2 * t] = 0u;
+    __syncthreads();
+    for (int i = t; i < n_cand; i += kResolveThreads) {
+      const uint32_t key = cand(i)[0];
+      if ((key >> 10) == pre22) atomicAdd(&S.h[key & 1023u], 1u);
+    }
+    __syncthreads();
+    hb[0] = S.h[kBins23 - 1 - 2 * t];
+    hb[1] = S.h[kBins23 - 2 - 2 * t];
+    int above3, n_eq;
+    const uint32_t b3 = (uint32_t)find_bin_n<kResolveWaves, 2>(hb, kBins23, k2, wsum, res[1], above3, n_eq);
+    const uint32_t kstar = (pre22 << 10) | b3;
+    ties = k2 - above3;
+    // per chunk: candidates above and equal to K* (a candidate's chunk is its
+    // position / 2048); this chunk's own go to its bitmaps
+    for (int i = t; i < n_cand; i += kResolveThreads) {
+      const u32x2 e = cand(i);
+      const int c = (int)(e[1] >> 11);
+      if (e[0] > kstar) {
+        atomicAdd(&S.gt[c], 1);
+        if (c == w) atomicOr(&S.bm[(e[1] & (kChunk - 1)) >> 5], 1u << (e[1] & 31));
+      } else if (e[0] == kstar) {
+        atomicAdd(&S.eq[c], 1);
+        if (c == w) atomicOr(&S.tie[(e[1] & (kChunk - 1)) >> 5], 1u << (e[1] & 31));
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
   // ---- wave 0: the chunk's output offset and its share of the ties, then its
   // positions in order (lane = bitmap word of 32 positions)
   if (wave == 0) {
-    const int eq = live_ln ? S.eq[lane] : 0;
+    const int eq = live_ln ? S.eq[lane] + x_eq : 0;
     const int eq_before = wave_inclusive_scan(eq) - eq;
     const int take = min(eq, max(0, ties - eq_before));  // ties taken in this chunk
-    const int sel = live_ln ? S.lo[lane] + S.gt[lane] + take : 0;
+    const int sel = live_ln ? S.lo[lane] + S.gt[lane] + x_gt + take : 0;
     const int off = wave_inclusive_scan(sel) - sel;
     const int my_off = __shfl(off, w), my_take = __shfl(take, w);
     // this chunk's ties: the first my_take tie bits in position order
-    uint32_t tw = S.tie[lane];
+    uint32_t tw = S.tie[lane] | x_tie;
     const int tc = __popc(tw);
     int rank = wave_inclusive_scan(tc) - tc;
     uint32_t x = tw;
@@ -473,7 +529,7 @@ __global__ __launch_bounds__(kResolveThreads, 2) void select_resolve_kernel(SelA
       ++rank;
       x &= x - 1u;
     }
-    uint32_t word = S.bm[lane] | tw;
+    uint32_t word = S.bm[lane] | x_bm | tw;
     const int cnt = __popc(word);
     int idx = wave_inclusive_scan(cnt) - cnt;
     while (word) {

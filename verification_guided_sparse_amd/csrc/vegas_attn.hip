@@ -308,9 +308,11 @@ __global__ __launch_bounds__(kThreads) void combine_stage_kernel(AttnArgs a, Sel
   combine_block<D, RPB>(a, c % ncomb_x, (c / ncomb_x) % Hkv, c / (ncomb_x * Hkv));
 }
 
+// rpb: rows per combine block (combine_rows_per_block).
 template <int D>
-void launch_combine_stage(int rpb, const AttnArgs &a, const SelArgs &s, const StageWs &o, int ncomb_x,
-                          int nstage_x, hipStream_t st) {
+void launch_combine_stage(int rpb, const AttnArgs &a, const SelArgs &s, const StageWs &o, int nstage_x,
+                          hipStream_t st) {
+  const int ncomb_x = (a.rows + rpb - 1) / rpb;
   const dim3 grid(nstage_x * s.batch + ncomb_x * a.num_kv_heads * a.batch);
   switch (rpb) {
     case 1: hipLaunchKernelGGL((combine_stage_kernel<D, 1>), grid, dim3(kThreads), 0, st, a, s, o, ncomb_x, nstage_x); break;
@@ -634,9 +636,8 @@ vg_status vg_verify_select(const vg_shape *shape, const void *q, const void *k_c
   const vg_status st = launch_attention(shape, p, a, static_cast<char *>(verify_ws), hs, false);
   if (st != VG_OK) return st;
   const int rpb = combine_rows_per_block(shape, p);
-  const int ncomb_x = (p.rows + rpb - 1) / rpb;
-  if (shape->head_dim == 128) launch_combine_stage<128>(rpb, a, sa, o, ncomb_x, sp.chunks, hs);
-  else launch_combine_stage<64>(rpb, a, sa, o, ncomb_x, sp.chunks, hs);
+  if (shape->head_dim == 128) launch_combine_stage<128>(rpb, a, sa, o, sp.chunks, hs);
+  else launch_combine_stage<64>(rpb, a, sa, o, sp.chunks, hs);
   hipLaunchKernelGGL(select_resolve_kernel, dim3(sp.chunks, B), dim3(kResolveThreads), 0, hs, sa, o);
   return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
 }
