@@ -159,10 +159,11 @@ typedef struct {
   double *out, *logits, *group, *logits_all;
 } verify_ctx;
 
+/* One thread unit: every verify row of query head h of sequence b. */
 static void *verify_unit(void *vctx, int unit) {
   verify_ctx *c = (verify_ctx *)vctx;
-  int b = unit / c->Hkv, g = unit % c->Hkv;
-  int G = c->Hq / c->Hkv, R = c->gamma + 1, D = c->D;
+  int b = unit / c->Hq, h = unit % c->Hq;
+  int G = c->Hq / c->Hkv, R = c->gamma + 1, D = c->D, g = h / G;
   long long P = c->prefix_len[b];
   long long N = P + R;
   long long *slots = (long long *)malloc(sizeof(long long) * (size_t)N);
@@ -171,57 +172,60 @@ static void *verify_unit(void *vctx, int unit) {
   void *bad = NULL;
   if (!slots || !l || !qv) { bad = (void *)1; goto done; }
   for (long long j = 0; j < N; ++j) slots[j] = slot_of(c->page_table, c->max_pages, c->ps, b, j);
-  for (int hh = 0; hh < G; ++hh) {
-    int h = g * G + hh;
-    for (int r = 0; r < R; ++r) {
-      for (int d = 0; d < D; ++d)
-        qv[d] = load_elem(c->q, c->dtype, (((size_t)b * R + r) * c->Hq + h) * (size_t)D + d);
-      /* Verification is standard full attention (Vegas, section 2, core
-       * mechanism, verification phase); causal among the new rows: row r sees
-       * positions 0 .. P + r. */
-      double *o = c->out + (((size_t)b * R + r) * c->Hq + h) * (size_t)D;
-      if (attend(qv, D, c->dtype, c->scale, c->k_cache, c->v_cache, c->Hkv, g, slots, P + r + 1,
-                 l, o) != ORACLE_OK) {
-        bad = (void *)1;
-        goto done;
-      }
-      /* Collect-2-Query (section 2.B): only the first draft row and the bonus
-       * row export their pre-softmax logits (section 3, kernel instrumentation),
-       * over the prefix positions j < P. */
-      if (c->logits) {
-        if (r == 0)
-          memcpy(c->logits + (((size_t)b * 2 + 0) * c->Hq + h) * (size_t)c->max_prefix, l,
-                 sizeof(double) * (size_t)P);
-        if (r == c->gamma)
-          memcpy(c->logits + (((size_t)b * 2 + 1) * c->Hq + h) * (size_t)c->max_prefix, l,
-                 sizeof(double) * (size_t)P);
-      }
-      /* Full collection: the selection objective as written sums every verify row. */
-      if (c->logits_all)
-        memcpy(c->logits_all + (((size_t)b * R + r) * c->Hq + h) * (size_t)c->max_prefix, l,
+  for (int r = 0; r < R; ++r) {
+    for (int d = 0; d < D; ++d)
+      qv[d] = load_elem(c->q, c->dtype, (((size_t)b * R + r) * c->Hq + h) * (size_t)D + d);
+    /* Verification is standard full attention (Vegas, section 2, core
+     * mechanism, verification phase); causal among the new rows: row r sees
+     * positions 0 .. P + r. */
+    double *o = c->out + (((size_t)b * R + r) * c->Hq + h) * (size_t)D;
+    if (attend(qv, D, c->dtype, c->scale, c->k_cache, c->v_cache, c->Hkv, g, slots, P + r + 1,
+               l, o) != ORACLE_OK) {
+      bad = (void *)1;
+      goto done;
+    }
+    /* Collect-2-Query (section 2.B): only the first draft row and the bonus
+     * row export their pre-softmax logits (section 3, kernel instrumentation),
+     * over the prefix positions j < P. */
+    if (c->logits) {
+      if (r == 0)
+        memcpy(c->logits + (((size_t)b * 2 + 0) * c->Hq + h) * (size_t)c->max_prefix, l,
+               sizeof(double) * (size_t)P);
+      if (r == c->gamma)
+        memcpy(c->logits + (((size_t)b * 2 + 1) * c->Hq + h) * (size_t)c->max_prefix, l,
                sizeof(double) * (size_t)P);
     }
-  }
-  if (c->group) {
-    /* group[b][g][j] = sum over the G query heads of KV head g of the two
-     * exported rows' logits. */
-    if (!c->logits) { bad = (void *)1; goto done; }
-    double *gs = c->group + ((size_t)b * c->Hkv + g) * (size_t)c->max_prefix;
-    for (long long j = 0; j < P; ++j) {
-      double s = 0.0;
-      for (int hh = 0; hh < G; ++hh) {
-        int h = g * G + hh;
-        s += c->logits[(((size_t)b * 2 + 0) * c->Hq + h) * (size_t)c->max_prefix + j];
-        s += c->logits[(((size_t)b * 2 + 1) * c->Hq + h) * (size_t)c->max_prefix + j];
-      }
-      gs[j] = s;
-    }
+    /* Full collection: the selection objective as written sums every verify row. */
+    if (c->logits_all)
+      memcpy(c->logits_all + (((size_t)b * R + r) * c->Hq + h) * (size_t)c->max_prefix, l,
+             sizeof(double) * (size_t)P);
   }
 done:
   free(slots);
   free(l);
   free(qv);
   return bad;
+}
+
+/* One thread unit: the group export of KV head g of sequence b (after every
+ * head's logits are written):  group[b][g][j] = sum over the G query heads of
+ * KV head g of the two exported rows' logits. */
+static void *group_unit(void *vctx, int unit) {
+  verify_ctx *c = (verify_ctx *)vctx;
+  int b = unit / c->Hkv, g = unit % c->Hkv;
+  int G = c->Hq / c->Hkv;
+  long long P = c->prefix_len[b];
+  double *gs = c->group + ((size_t)b * c->Hkv + g) * (size_t)c->max_prefix;
+  for (long long j = 0; j < P; ++j) {
+    double s = 0.0;
+    for (int hh = 0; hh < G; ++hh) {
+      int h = g * G + hh;
+      s += c->logits[(((size_t)b * 2 + 0) * c->Hq + h) * (size_t)c->max_prefix + j];
+      s += c->logits[(((size_t)b * 2 + 1) * c->Hq + h) * (size_t)c->max_prefix + j];
+    }
+    gs[j] = s;
+  }
+  return NULL;
 }
 
 /* Full causal attention of rows 0..gamma over keys [0, P_b + r] of each
@@ -245,9 +249,12 @@ int oracle_verify(int B, int Hq, int Hkv, int D, int page_size, int max_pages, i
         (n + page_size - 1) / page_size > max_pages)
       return ORACLE_EINVAL;
   }
+  if (group && !logits) return ORACLE_EINVAL;
   verify_ctx c = {B, Hq, Hkv, D, page_size, max_pages, dtype, gamma, max_prefix, scale,
                   q, k_cache, v_cache, page_table, prefix_len, out, logits, group, logits_all};
-  return run_units(B * Hkv, verify_unit, &c, nthreads);
+  int rc = run_units(B * Hq, verify_unit, &c, nthreads);
+  if (rc == ORACLE_OK && group) rc = run_units(B * Hkv, group_unit, &c, nthreads);
+  return rc;
 }
 
 /* --------------------------------------------------------------- aggregate */
@@ -341,10 +348,11 @@ typedef struct {
   double *out;
 } sparse_ctx;
 
+/* One thread unit: every draft row of query head h of sequence b. */
 static void *sparse_unit(void *vctx, int unit) {
   sparse_ctx *c = (sparse_ctx *)vctx;
-  int b = unit / c->Hkv, g = unit % c->Hkv;
-  int G = c->Hq / c->Hkv, D = c->D;
+  int b = unit / c->Hq, h = unit % c->Hq;
+  int G = c->Hq / c->Hkv, D = c->D, g = h / G;
   long long cnt = c->sel_count[b], t0 = c->tail_start[b], tl = c->tail_len[b];
   long long nmax = cnt + tl;
   long long *slots = (long long *)malloc(sizeof(long long) * (size_t)(nmax > 0 ? nmax : 1));
@@ -361,18 +369,15 @@ static void *sparse_unit(void *vctx, int unit) {
                        c->sel_pos[(size_t)b * c->max_k + i]);
   for (long long i = 0; i < tl; ++i)
     slots[cnt + i] = slot_of(c->page_table, c->max_pages, c->ps, b, t0 + i);
-  for (int hh = 0; hh < G; ++hh) {
-    int h = g * G + hh;
-    for (int row = 0; row < c->n_q; ++row) {
-      for (int d = 0; d < D; ++d)
-        qv[d] = load_elem(c->q, c->dtype, (((size_t)b * c->n_q + row) * c->Hq + h) * (size_t)D + d);
-      long long n = cnt + tl - c->n_q + row + 1;
-      double *o = c->out + (((size_t)b * c->n_q + row) * c->Hq + h) * (size_t)D;
-      if (attend(qv, D, c->dtype, c->scale, c->k_cache, c->v_cache, c->Hkv, g, slots, n, l, o) !=
-          ORACLE_OK) {
-        bad = (void *)1;
-        goto done;
-      }
+  for (int row = 0; row < c->n_q; ++row) {
+    for (int d = 0; d < D; ++d)
+      qv[d] = load_elem(c->q, c->dtype, (((size_t)b * c->n_q + row) * c->Hq + h) * (size_t)D + d);
+    long long n = cnt + tl - c->n_q + row + 1;
+    double *o = c->out + (((size_t)b * c->n_q + row) * c->Hq + h) * (size_t)D;
+    if (attend(qv, D, c->dtype, c->scale, c->k_cache, c->v_cache, c->Hkv, g, slots, n, l, o) !=
+        ORACLE_OK) {
+      bad = (void *)1;
+      goto done;
     }
   }
 done:
@@ -405,5 +410,5 @@ int oracle_sparse(int B, int Hq, int Hkv, int D, int page_size, int max_pages, i
   }
   sparse_ctx c = {B, Hq, Hkv, D, page_size, max_pages, dtype, n_q, max_k, scale,
                   q, k_cache, v_cache, page_table, sel_pos, sel_count, tail_start, tail_len, out};
-  return run_units(B * Hkv, sparse_unit, &c, nthreads);
+  return run_units(B * Hq, sparse_unit, &c, nthreads);
 }

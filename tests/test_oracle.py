@@ -247,6 +247,22 @@ def test_page_permutation_invariance():
         assert np.array_equal(x, y)
 
 
+def test_thread_count_does_not_change_results():
+    """The oracle's thread units (one per sequence and query head, then one per
+    sequence and KV head for the group export) each compute a fixed set of
+    outputs in a fixed order: one thread and many give bit-identical results."""
+    c = _tiny(prefix=(77, 40), gamma=3, hq=8, hkv=2)
+    one = oracle.verify(c.q, c.k_cache, c.v_cache, c.page_table, c.prefix_len, 3, c.scale, nthreads=1)
+    many = oracle.verify(c.q, c.k_cache, c.v_cache, c.page_table, c.prefix_len, 3, c.scale, nthreads=7)
+    for x, y in zip(one[:3], many[:3]):
+        assert np.array_equal(x, y)
+    s = oracle.aggregate(one[2], c.prefix_len)
+    pos, _, cnt = oracle.topk(s, c.prefix_len, np.array([9, 5]), page_table=c.page_table)
+    args = (np.ascontiguousarray(c.q_draft[1][:, None]), c.k_cache, c.v_cache, c.page_table, pos, cnt,
+            c.prefix_len, np.array([2, 2], np.int32), c.scale)
+    assert np.array_equal(oracle.sparse(*args, nthreads=1), oracle.sparse(*args, nthreads=5))
+
+
 def test_closed_forms():
     case = _tiny(dtype="f32", prefix=(20,), gamma=2, hq=2, hkv=1, d=8)
     # all keys equal -> uniform weights -> mean of the visible values
