@@ -5,18 +5,28 @@ stack of the configured layer (default: the Qwen3-8B-shaped layer at 128K
 context, gamma = 6, k = 4% of the prefix):
 
     for s in 0..gamma-1:  for each layer: sparse draft attention (draft step s)
-    for each layer:       verify attention + group-sum export, aggregation with
-                          the fused first radix pass, exact top-k
+    for each layer:       verify attention with the group-sum export,
+                          aggregation and exact top-k (one vg_verify_select call)
 
 Each layer has its own KV cache copy in HBM, so no layer's data is still in
 the 256 MB MALL when it is read again: every byte counted below is an HBM
 byte.  Inputs are seeded synthetic tensors, resident in HBM before timing.
 
+Timing: the draft steps of all layers are one HIP graph and the verify calls
+another; a timed step replays the two back to back on one stream, with HIP
+events before, between and after them, so every step gives its own duration
+and its two segments' durations.  Two more timed loops of the same shape
+measure, in the same place in the step, the verify call on its own (then the
+selection call) and the verify call without export: they give the verify
+call's in-step duration (the roofline's dominant kernel) and the selection's
+overhead against verify.
+
 Printed: one JSON line with the whole-step achieved HBM GB/s (algorithmic
-bytes / time), ms per step, per-layer us per iteration, the roofline of the
-dominant kernel (verify attention, timed with HIP events around every verify
-call inside the timed region) and the fp64 CPU oracle timed on a bounded
-sample of the same workload on the host cores.
+bytes / mean step time), the step-time median / p10 / p90, per-layer us per
+iteration, the in-step fractions of HBM peak of the verify call and of the
+draft call, the selection overhead, per-workload figures for the other
+configurations, and the fp64 CPU oracle timed on a bounded sample of the
+same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -103,17 +113,124 @@ def cpu_baseline(c, export, nthreads, min_seconds=10.0):
             return elapsed / n, n
 
 
+def host_info():
+    """CPU model and online CPU count of the host (for the CPU baseline)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count() or 1
+
+
+def build_layers(c, L, kernel):
+    """L layer copies of workload c, each with its own KV cache in HBM, and one
+    eager iteration each (the first draft step needs a selection)."""
+    import torch
+    from verification_guided_sparse_amd.runner import DeviceCase
+    dev = torch.device("cuda:0")
+    layers = [DeviceCase(c, device=dev, kernel=kernel)]
+    for _ in range(L - 1):
+        layers.append(DeviceCase(c, device=dev, kernel=kernel, like=layers[0]))
+    return layers
+
+
+def pct(xs, q):
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
+def segment_loop(graphs, steps):
+    """Replays the graphs in order, `steps` times, on the current stream with a
+    HIP event before, between and after them; returns per-step per-segment
+    milliseconds ([steps][len(graphs)]) and the total milliseconds."""
+    import torch
+    n = len(graphs)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps * n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for k in range(steps):
+        for i, g in enumerate(graphs):
+            g.replay()
+            ev[k * n + i + 1].record()
+    torch.cuda.synchronize()
+    seg = [[ev[k * n + i].elapsed_time(ev[k * n + i + 1]) for i in range(n)] for k in range(steps)]
+    return seg, ev[0].elapsed_time(ev[steps * n])
+
+
+def measure(c, layers, export, steps, warmup):
+    """The timed step and the in-step segments of one workload (see the module
+    docstring).  Durations in us per call (per layer), unless named _ms."""
+    L, g = len(layers), max(c.gamma, 1)
+    g_draft = capture(lambda: [lc.sparse(step=s) for s in range(c.gamma) for lc in layers])
+    if export == "group":
+        g_vsel = capture(lambda: [lc.verify_select() for lc in layers])
+    else:
+        g_vsel = capture(lambda: [(lc.verify(export=export), lc.select(src=export)) for lc in layers])
+    g_verify = capture(lambda: [lc.verify(export=export) for lc in layers])
+    g_select = capture(lambda: [lc.select(src=export) for lc in layers])
+    g_none = capture(lambda: [lc.verify(export="none") for lc in layers])
+    for _ in range(warmup):
+        g_draft.replay()
+        g_vsel.replay()
+    t0 = time.perf_counter()
+    seg, total_ms = segment_loop([g_draft, g_vsel], steps)  # the timed steps
+    wall = time.perf_counter() - t0
+    step_ms = [sum(x) for x in seg]
+    seg_b, _ = segment_loop([g_draft, g_verify, g_select], steps)
+    seg_c, _ = segment_loop([g_draft, g_none], steps)
+    us = lambda xs, n: 1e3 * float(np.mean(xs)) / n
+    r = {
+        "ms_per_step": total_ms / steps,
+        "step_ms_median": pct(step_ms, 50), "step_ms_p10": pct(step_ms, 10), "step_ms_p90": pct(step_ms, 90),
+        "draft_us": us([x[0] for x in seg], g * L),
+        "verify_select_us": us([x[1] for x in seg], L),
+        "verify_us": us([x[1] for x in seg_b], L),
+        "verify_us_p10": 1e3 * pct([x[1] for x in seg_b], 10) / L,
+        "verify_us_p90": 1e3 * pct([x[1] for x in seg_b], 90) / L,
+        "select_us": us([x[2] for x in seg_b], L),
+        "verify_no_export_us": us([x[1] for x in seg_c], L),
+        "wall_s_timed": wall,
+    }
+    r["overhead_frac"] = (r["verify_select_us"] - r["verify_no_export_us"]) / r["verify_no_export_us"]
+    return r
+
+
+def workload_figures(c, r, export):
+    """Per-layer figures and fractions of the HBM peak from measure()'s result."""
+    ab = algorithmic_bytes(c, export)
+    draft_bytes = float(np.mean(ab["draft"])) if ab["draft"] else 0.0
+    verify_gbs = ab["verify"] / (r["verify_us"] * 1e-6) / 1e9
+    draft_gbs = draft_bytes / (r["draft_us"] * 1e-6) / 1e9 if r["draft_us"] > 0 else 0.0
+    return {
+        "us_per_iter": round(1e3 * r["ms_per_step"] / r["layers"], 2),
+        "verify_us_in_step": round(r["verify_us"], 2),
+        "verify_frac_in_step": round(verify_gbs / PEAK_HBM_GBS, 4),
+        "draft_us_in_step": round(r["draft_us"], 2),
+        "draft_frac_in_step": round(draft_gbs / PEAK_HBM_GBS, 4),
+        "verify_select_us_in_step": round(r["verify_select_us"], 2),
+        "verify_no_export_us_in_step": round(r["verify_no_export_us"], 2),
+        "overhead_frac": round(r["overhead_frac"], 4),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3_qwen3_128k")
     ap.add_argument("--layers", type=int, default=0, help="layer copies (0: enough to exceed the MALL)")
     ap.add_argument("--export", choices=["group", "raw"], default="group")
     ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--breakdown", action="store_true", help="also time every step separately")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the per-workload figures of the other configurations")
+    ap.add_argument("--other-workloads", default="c2_qwen3_32k,c4_ragged_b8,c5_gptoss_64k")
+    ap.add_argument("--breakdown", action="store_true", help="also time every call kind separately")
     ap.add_argument("--collection", action="store_true",
                     help="also time the logit export + aggregation for two rows (Collect-2-Query) "
                          "against every row (full collection)")
@@ -137,7 +254,6 @@ def main():
     import torch
     from verification_guided_sparse_amd import _binding as vg
     from verification_guided_sparse_amd import synth
-    from verification_guided_sparse_amd.runner import DeviceCase
 
     vg.lib()  # fail loudly if the HIP library is missing
     if args.sweep:
@@ -151,58 +267,16 @@ def main():
         L = args.layers
     print(f"[bench] {args.workload}: {L} layers, {layer_kv / 1e6:.1f} MB KV per layer, "
           f"export={args.export}, kernel={args.kernel}", file=sys.stderr, flush=True)
-
-    dev = torch.device("cuda:0")
-    layers = [DeviceCase(c, device=dev, kernel=kernel)]
-    for _ in range(L - 1):
-        layers.append(DeviceCase(c, device=dev, kernel=kernel, like=layers[0]))
-
-    def step():
-        for s in range(c.gamma):
-            for lc in layers:
-                lc.sparse(step=s)
-        for lc in layers:
-            if args.export == "group":
-                lc.verify_select()
-            else:
-                lc.verify(export=args.export)
-                lc.select(src=args.export)
-
-    # the first draft step needs a selection: run one eager iteration per layer
-    for lc in layers:
-        lc.iteration(export=args.export)
-    torch.cuda.synchronize()
-    # one step = one HIP graph (no host launch overhead inside the timed region)
-    g_step = capture(step)
-    g_verify = capture(lambda: [lc.verify(export=args.export) for lc in layers])
-    for _ in range(args.warmup):
-        g_step.replay()
-    torch.cuda.synchronize()
-
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    v_start, v_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record()
-    for k in range(args.steps):
-        g_step.replay()
-    t_end.record()
-    # the dominant kernel: every layer's verify call, back to back, same graph form
-    v_start.record()
-    for k in range(args.steps):
-        g_verify.replay()
-    v_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    verify_us = 1e3 * v_start.elapsed_time(v_end) / (args.steps * L)
+    layers = build_layers(c, L, kernel)
+    r = measure(c, layers, args.export, args.steps, args.warmup)
+    r["layers"] = L
+    fig = workload_figures(c, r, args.export)
+    print(f"[bench] {args.workload}: {json.dumps(fig)}", file=sys.stderr, flush=True)
 
     bytes_per_step = ab["total"] * L
-    value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
-    achieved = ab["verify"] / (verify_us * 1e-6) / 1e9
-    khash = kernel_source_hash()
-    traffic = measured_traffic(args.workload, khash)
+    value = bytes_per_step / (r["ms_per_step"] * 1e-3) / 1e9
+    achieved = ab["verify"] / (r["verify_us"] * 1e-6) / 1e9
+    traffic = measured_traffic(args.workload, kernel_source_hash())
 
     result = {
         "metric": METRIC,
@@ -211,7 +285,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -230,28 +304,58 @@ def main():
             "kernel": args.kernel,
             "parallelism": "single-gpu",
         },
-        "us_per_iter": round(1e3 * ms_per_step / L, 2),
+        "step_ms": {"median": round(r["step_ms_median"], 4), "p10": round(r["step_ms_p10"], 4),
+                    "p90": round(r["step_ms_p90"], 4)},
+        "us_per_iter": fig["us_per_iter"],
         "roofline": {
-            "kernel": "vg_verify_attention (attention kernel + its combine kernel)",
+            "kernel": "vg_verify_attention (attention kernel + its combine kernel), in-step",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "verify_us": round(verify_us, 2),
+            "verify_us": round(r["verify_us"], 2),
+            "verify_us_p10": round(r["verify_us_p10"], 2),
+            "verify_us_p90": round(r["verify_us_p90"], 2),
             "algorithmic_bytes_per_launch": ab["verify"],
         },
-        "wall_s_timed": round(wall, 3),
+        "targets": {
+            "verify_frac_in_step": fig["verify_frac_in_step"],
+            "draft_frac_in_step": fig["draft_frac_in_step"],
+            "draft_us_in_step": fig["draft_us_in_step"],
+            "overhead_frac": fig["overhead_frac"],
+            "verify_select_us_in_step": fig["verify_select_us_in_step"],
+            "verify_no_export_us_in_step": fig["verify_no_export_us_in_step"],
+            "select_us_in_step_separate_call": round(r["select_us"], 2),
+        },
+        "wall_s_timed": round(r["wall_s_timed"], 3),
     }
 
     if args.breakdown:
         result["breakdown_us"] = breakdown(layers, c, args.export)
     if args.collection:
         result["collection_us"] = collection(layers)
+    del layers
+    torch.cuda.empty_cache()
+
+    if not args.no_other_workloads:
+        others = {}
+        for wl in [w for w in args.other_workloads.split(",") if w and w != args.workload]:
+            cw = synth.make_case(wl)
+            Lw, _ = layer_count(cw, algorithmic_bytes(cw, args.export))
+            lw = build_layers(cw, Lw, kernel)
+            rw = measure(cw, lw, args.export, min(args.steps, 10), 2)
+            rw["layers"] = Lw
+            others[wl] = dict(workload_figures(cw, rw, args.export), layers=Lw)
+            print(f"[bench] {wl}: {json.dumps(others[wl])}", file=sys.stderr, flush=True)
+            del lw
+            torch.cuda.empty_cache()
+        result["other_workloads"] = others
 
     if not args.no_cpu_baseline:
-        nthreads = min(16, os.cpu_count() or 1)
+        model, ncpu = host_info()
+        nthreads = min(16, ncpu)  # the host's CPU share per GPU
         t, n_it = cpu_baseline(c, args.export, nthreads)
         result["cpu_baseline"] = {
             "value": round(ab["total"] / t / 1e9, 4),
@@ -260,6 +364,17 @@ def main():
             "kind": "oracle",
             "sample": f"{n_it} full {args.workload} layer iterations (verify, aggregate, top-k, "
                       f"{c.gamma} draft steps) in fp64, {t:.2f} s each",
+            "host_cpus": ncpu,
+            "cpu_model": model,
+        }
+        c2 = synth.make_case("c2_qwen3_32k")
+        t1, n1 = cpu_baseline(c2, args.export, 1, min_seconds=8.0)
+        result["cpu_baseline_1thread"] = {
+            "value": round(algorithmic_bytes(c2, args.export)["total"] / t1 / 1e9, 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n1} full c2_qwen3_32k layer iterations in fp64 on one thread, {t1:.2f} s each",
         }
     print(json.dumps(result), flush=True)
 
