@@ -222,7 +222,8 @@ vg_status vg_topk_select(int32_t batch, const float *scores, int32_t max_prefix,
  *   workspace: sized by vg_topk_workspace_size(batch, max_prefix), zero-filled
  *       once before first use (the call leaves it zero-filled again).
  * With max_prefix <= 131072 and even, and page_size 16 (or sel_slot null), the
- * whole selection runs in one kernel launch; otherwise in three.
+ * selection runs in two kernel launches (per-chunk staging, then the exact
+ * threshold and the output); otherwise in three (radix passes).
  */
 vg_status vg_aggregate_topk_select(int32_t batch, const float *src, int32_t src_rows, int32_t src_heads,
                                    const int32_t *prefix_len, int32_t max_prefix, float *scores,
