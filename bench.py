@@ -241,9 +241,18 @@ def main():
     ap.add_argument("--sweep-k-pcts", default="1,2,4,8,16")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (HBM byte-counter calibration)")
+    ap.add_argument("--cpu-steps", default="", metavar="WORKLOADS",
+                    help="only time the fp64 oracle's steps for these workloads (comma-separated) "
+                         "on min(16, host CPUs) threads, and for the 2K and 32K ones also on one "
+                         "thread (no GPU use)")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.cpu_steps:
+        wls = [w for w in args.cpu_steps.split(",") if w]
+        cpu_steps(wls, [min(16, host_info()[1])])
+        cpu_steps([w for w in wls if w in ("c1_tiny", "c2_qwen3_32k")], [1])
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -377,6 +386,36 @@ def main():
             "sample": f"{n1} full c2_qwen3_32k layer iterations in fp64 on one thread, {t1:.2f} s each",
         }
     print(json.dumps(result), flush=True)
+
+
+def cpu_steps(workloads, threads):
+    """The fp64 oracle's time per step (verify with the export, aggregation,
+    top-k, one draft step) for each workload, on each thread count: one run of
+    each step, wall clock."""
+    import oracle
+    from verification_guided_sparse_amd import synth
+    model, ncpu = host_info()
+    rows = []
+    for wl in workloads:
+        c = synth.make_case(wl)
+        for nt in threads:
+            t0 = time.perf_counter()
+            out, logits, group, _ = oracle.verify(c.q, c.k_cache, c.v_cache, c.page_table, c.prefix_len,
+                                                  c.gamma, c.scale, nthreads=nt)
+            t1 = time.perf_counter()
+            s = oracle.aggregate(group, c.prefix_len)
+            t2 = time.perf_counter()
+            pos, slot, cnt = oracle.topk(s, c.prefix_len, c.k, page_table=c.page_table)
+            t3 = time.perf_counter()
+            oracle.sparse(np.ascontiguousarray(c.q_draft[0][:, None]), c.k_cache, c.v_cache, c.page_table,
+                          pos, cnt, c.prefix_len, np.full(c.batch, 1, np.int32), c.scale, nthreads=nt)
+            t4 = time.perf_counter()
+            row = {"workload": wl, "threads": nt, "verify_s": round(t1 - t0, 3),
+                   "aggregate_ms": round(1e3 * (t2 - t1), 2), "topk_ms": round(1e3 * (t3 - t2), 2),
+                   "draft_step_ms": round(1e3 * (t4 - t3), 2), "host_cpus": ncpu, "cpu_model": model}
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+    return rows
 
 
 def calibrate_copy(nbytes):
