@@ -382,10 +382,10 @@ __global__ __launch_bounds__(kResolveThreads, 2) void select_resolve_kernel(SelA
   const bool cached = n_cand <= kResolveCache;
   const u32x2 *stg = a.ws.cand + (size_t)b * a.max_prefix;
   // ---- round 3: this chunk's entries above b1 (their positions), and every
-  // candidate into the LDS cache (wave v takes items v, v + 8, ...,
-  // kItemBatch of them per batch; an item's chunk and offsets are
-  // wave-uniform).  The first own load and the first batch of items are in
-  // flight together; more of either is rare.
+  // candidate into the LDS cache and the histogram of its key bits [10, 20)
+  // (wave v takes items v, v + 8, ..., kItemBatch of them per batch; an
+  // item's chunk and offsets are wave-uniform).  The first own load and the
+  // first batch of items are in flight together; more of either is rare.
   {
     const int lo_own = __builtin_amdgcn_readlane(lo_ln, w);
     const uint32_t *own_pos = reinterpret_cast<const uint32_t *>(stg + (size_t)w * kChunk) + 1;
@@ -412,8 +412,12 @@ __global__ __launch_bounds__(kResolveThreads, 2) void select_resolve_kernel(SelA
         v[q] = stg[ok ? (size_t)c * kChunk + __builtin_amdgcn_readlane(lo_ln, c) + i : 0];
       }
 #pragma unroll
-      for (int q = 0; q < kItemBatch; ++q)
-        if (dst[q] >= 0) S.cache[dst[q]] = v[q];
+      for (int q = 0; q < kItemBatch; ++q) {
+        if (dst[q] >= 0) {
+          S.cache[dst[q]] = v[q];
+          atomicAdd(&S.h[(v[q][0] >> 10) & 1023u], 1u);  // the histogram of key bits [10, 20)
+        }
+      }
     };
     if (wave < n_it) item_batch(wave);
     mark_own(t, up0);
@@ -428,9 +432,12 @@ __global__ __launch_bounds__(kResolveThreads, 2) void select_resolve_kernel(SelA
     while (S.cand_off[c + 1] <= i) ++c;
     return stg[(size_t)c * kChunk + S.lo[c] + (i - S.cand_off[c])];
   };
-  // ---- K* from the candidates: bits [10, 20), then [0, 10)
-  for (int i = t; i < n_cand; i += kResolveThreads) atomicAdd(&S.h[(cand(i)[0] >> 10) & 1023u], 1u);
-  __syncthreads();
+  // ---- K* from the candidates: bits [10, 20) (histogram built as the cached
+  // candidates arrived), then [0, 10)
+  if (!cached) {
+    for (int i = t; i < n_cand; i += kResolveThreads) atomicAdd(&S.h[(cand(i)[0] >> 10) & 1023u], 1u);
+    __syncthreads();
+  }
   uint32_t hb[2] = {S.h[kBins23 - 1 - 2 * t], S.h[kBins23 - 2 - 2 * t]};
   int above2, n_b2;
   const uint32_t b2 = (uint32_t)find_bin_n<kResolveWaves, 2>(hb, kBins23, k1, wsum, res[0], above2, n_b2);
