@@ -156,7 +156,7 @@ struct WaveState {
   int xbase[NT];         // 0, or the row r when every row is exported
 };
 
-template <int D, int NT>
+template <int D, int NT, bool RAW>
 __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D> &T,
                                              KStage<D> &ks_sm, const AttnArgs &a, int b, int g,
                                              const SeqList &s, int e0, int e_end, int lane,
@@ -201,7 +201,7 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
   // Logit export (verify): rows 0 and gamma (or every row), entries below the
   // prefix length.
   if (do_export && e0 < s.p_export) {
-    if (a.logits) {
+    if (RAW && a.logits) {
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) {
         if (W.xrow[rt]) {
@@ -329,7 +329,9 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
   }
 }
 
-template <int D, int NT, int PF, bool SPARSE>
+// RAW: the raw-logit export is compiled in (verify calls that export raw
+// logits); without it the kernel exports group sums only, or nothing.
+template <int D, int NT, int PF, bool SPARSE, bool RAW = false>
 __global__ __launch_bounds__(kThreads, attn_occupancy(D, NT, PF, SPARSE))
 void attn_mfma_kernel(AttnArgs a_in) {
   AttnArgs a = a_in;
@@ -447,21 +449,21 @@ void attn_mfma_kernel(AttnArgs a_in) {
       for (; j + 2 * PF <= nw; j += PF) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
-          compute_tile<D, NT>(W, T[u], lds.kst[wave], a, b, g, s, e_of(j + u), c1, lane, do_export, vec_export);
+          compute_tile<D, NT, RAW>(W, T[u], lds.kst[wave], a, b, g, s, e_of(j + u), c1, lane, do_export, vec_export);
           load_tile<D>(T[u], a, b, s, e_of(j + u + PF), g, lane, slot_sm, c0, c1);
         }
       }
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
         if (j + u < nw) {
-          compute_tile<D, NT>(W, T[u], lds.kst[wave], a, b, g, s, e_of(j + u), c1, lane, do_export, vec_export);
+          compute_tile<D, NT, RAW>(W, T[u], lds.kst[wave], a, b, g, s, e_of(j + u), c1, lane, do_export, vec_export);
           if (j + u + PF < nw) load_tile<D>(T[u], a, b, s, e_of(j + u + PF), g, lane, slot_sm, c0, c1);
         }
       }
 #pragma unroll
       for (int u = 0; u < PF; ++u)
         if (j + PF + u < nw)
-          compute_tile<D, NT>(W, T[u], lds.kst[wave], a, b, g, s, e_of(j + PF + u), c1, lane, do_export, vec_export);
+          compute_tile<D, NT, RAW>(W, T[u], lds.kst[wave], a, b, g, s, e_of(j + PF + u), c1, lane, do_export, vec_export);
     }
 
     __syncthreads();  // the K staging area becomes the merge area

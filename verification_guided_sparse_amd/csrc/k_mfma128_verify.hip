@@ -7,7 +7,10 @@ namespace vg {
 
 template <int NT>
 static void launch_nt(const AttnArgs &a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_mfma_kernel<128, NT, verify_pf(128, NT), false>), grid, dim3(kThreads), 0, st, a);
+  if (a.logits)
+    hipLaunchKernelGGL((attn_mfma_kernel<128, NT, verify_pf(128, NT), false, true>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<128, NT, verify_pf(128, NT), false>), grid, dim3(kThreads), 0, st, a);
 }
 
 void launch_mfma128_verify(int nt, const AttnArgs &a, dim3 grid, hipStream_t st) {

@@ -7,7 +7,10 @@ namespace vg {
 
 template <int NT>
 static void launch_nt(const AttnArgs &a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_mfma_kernel<64, NT, verify_pf(64, NT), false>), grid, dim3(kThreads), 0, st, a);
+  if (a.logits)
+    hipLaunchKernelGGL((attn_mfma_kernel<64, NT, verify_pf(64, NT), false, true>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<64, NT, verify_pf(64, NT), false>), grid, dim3(kThreads), 0, st, a);
 }
 
 void launch_mfma64_verify(int nt, const AttnArgs &a, dim3 grid, hipStream_t st) {

@@ -516,52 +516,50 @@ __global__ __launch_bounds__(kResolveThreads, 2) void select_resolve_kernel(SelA
     }
     __syncthreads();
   }
-  // ---- wave 0: the chunk's output offset and its share of the ties, then its
-  // positions in order (lane = bitmap word of 32 positions)
-  if (wave == 0) {
-    const int eq = live_ln ? S.eq[lane] + x_eq : 0;
-    const int eq_before = wave_inclusive_scan(eq) - eq;
-    const int take = min(eq, max(0, ties - eq_before));  // ties taken in this chunk
-    const int sel = live_ln ? S.lo[lane] + S.gt[lane] + x_gt + take : 0;
-    const int off = wave_inclusive_scan(sel) - sel;
-    const int my_off = __shfl(off, w), my_take = __shfl(take, w);
-    // this chunk's ties: the first my_take tie bits in position order
-    uint32_t tw = S.tie[lane] | x_tie;
-    const int tc = __popc(tw);
-    int rank = wave_inclusive_scan(tc) - tc;
-    uint32_t x = tw;
-    while (x) {
-      const uint32_t bit = x & (~x + 1u);
-      if (rank >= my_take) tw &= ~bit;
-      ++rank;
-      x &= x - 1u;
-    }
-    uint32_t word = S.bm[lane] | x_bm | tw;
-    const int cnt = __popc(word);
-    int idx = wave_inclusive_scan(cnt) - cnt;
-    while (word) {
-      const int bit = __ffs(word) - 1;
-      word &= word - 1u;
-      S.out[idx++] = w * kChunk + 32 * lane + bit;
-    }
-    if (lane == 63) {
-      S.meta[3] = my_off;
-      S.meta[4] = idx;  // this chunk's selected count
-    }
+  // ---- wave 0 (the others are done): the chunk's output offset and its
+  // share of the ties, its positions in order (lane = bitmap word of 32
+  // positions), then their writes
+  if (wave != 0) return;
+  const int eq = live_ln ? S.eq[lane] + x_eq : 0;
+  const int eq_before = wave_inclusive_scan(eq) - eq;
+  const int take = min(eq, max(0, ties - eq_before));  // ties taken in this chunk
+  const int sel = live_ln ? lo_ln + S.gt[lane] + x_gt + take : 0;
+  const int off = wave_inclusive_scan(sel) - sel;
+  const int my_off = __shfl(off, w), my_take = __shfl(take, w);
+  // this chunk's ties: the first my_take tie bits in position order
+  uint32_t tw = S.tie[lane] | x_tie;
+  const int tc = __popc(tw);
+  int rank = wave_inclusive_scan(tc) - tc;
+  uint32_t x = tw;
+  while (x) {
+    const uint32_t bit = x & (~x + 1u);
+    if (rank >= my_take) tw &= ~bit;
+    ++rank;
+    x &= x - 1u;
   }
-  __syncthreads();
-  const int my_off = S.meta[3], n_own = S.meta[4];
+  uint32_t word = S.bm[lane] | x_bm | tw;
+  const int cnt = __popc(word);
+  int idx = wave_inclusive_scan(cnt) - cnt;
+  const int n_own = __builtin_amdgcn_readlane(idx + cnt, 63);  // this chunk's selected count
+  while (word) {
+    const int bit = __ffs(word) - 1;
+    word &= word - 1u;
+    S.out[idx++] = w * kChunk + 32 * lane + bit;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   int32_t *pos_row = a.sel_pos + (size_t)b * a.max_k;
   int32_t *slot_row = want_slots ? a.sel_slot + (size_t)b * a.max_k : nullptr;
-  for (int j = t; j < n_own; j += kResolveThreads) {
-    const int idx = my_off + j;
-    if (idx < a.max_k) {
+  for (int j = lane; j < n_own; j += kWave) {
+    const int i = my_off + j;
+    if (i < a.max_k) {
       const int pos = S.out[j];
-      pos_row[idx] = pos;
-      if (want_slots) slot_row[idx] = S.page[(pos & (kChunk - 1)) >> 4] * kPageSize + (pos & (kPageSize - 1));
+      pos_row[i] = pos;
+      if (want_slots) slot_row[i] = S.page[(pos & (kChunk - 1)) >> 4] * kPageSize + (pos & (kPageSize - 1));
     }
   }
-  if (w == 0 && t == 0) a.sel_count[b] = kk;
+  if (w == 0 && lane == 0) a.sel_count[b] = kk;
 }
 
 }  // namespace vg
