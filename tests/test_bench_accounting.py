@@ -67,3 +67,25 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and "--gpus 1" in r.stderr
+
+
+def test_workload_figures_from_segment_times():
+    """The per-workload figures divide the plan's bytes by the in-step segment
+    times: verify call bytes over the verify segment per layer, the mean draft
+    step's bytes over the draft segment per (step, layer), and the selection
+    overhead as (verify+select - verify without export) / verify without export."""
+    c = synth.make_case(synth.CONFIGS["c3_qwen3_128k"])
+    ab = bench.algorithmic_bytes(c, "group")
+    r = {"ms_per_step": 6.4, "layers": 36, "verify_us": 100.0, "draft_us": 10.0,
+         "verify_select_us": 110.0, "verify_no_export_us": 100.0, "overhead_frac": 0.1}
+    f = bench.workload_figures(c, r, "group")
+    assert f["us_per_iter"] == round(6400 / 36, 2)
+    assert f["verify_frac_in_step"] == round(ab["verify"] / 100e-6 / 1e9 / 8000, 4)
+    draft_mean = sum(ab["draft"]) / len(ab["draft"])
+    assert f["draft_frac_in_step"] == round(draft_mean / 10e-6 / 1e9 / 8000, 4)
+    assert f["overhead_frac"] == 0.1
+
+
+def test_percentiles_of_step_times():
+    xs = [5.0, 1.0, 4.0, 2.0, 3.0]
+    assert bench.pct(xs, 50) == 3.0 and bench.pct(xs, 10) == 1.4 and bench.pct(xs, 90) == 4.6
