@@ -74,7 +74,7 @@ struct KVTile {
 template <int D>
 struct KStage {
   static constexpr int kRowBytes = D * 2 + 16;
-  char rows[32 * kRowBytes];
+  alignas(16) char rows[32 * kRowBytes];
 };
 
 // Slots of a chunk of a piece's entries, staged in LDS once per workgroup so
