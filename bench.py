@@ -127,7 +127,7 @@ def host_info():
     return model, os.cpu_count() or 1
 
 
-def build_layers(c, L, kernel):
+def build_layers(c, L, kernel, export="group"):
     """L layer copies of workload c, each with its own KV cache in HBM, and one
     eager iteration each (the first draft step needs a selection)."""
     import torch
@@ -136,6 +136,9 @@ def build_layers(c, L, kernel):
     layers = [DeviceCase(c, device=dev, kernel=kernel)]
     for _ in range(L - 1):
         layers.append(DeviceCase(c, device=dev, kernel=kernel, like=layers[0]))
+    for lc in layers:
+        lc.iteration(export=export)
+    torch.cuda.synchronize()
     return layers
 
 
@@ -241,6 +244,9 @@ def main():
     ap.add_argument("--sweep-k-pcts", default="1,2,4,8,16")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (HBM byte-counter calibration)")
+    ap.add_argument("--verify-replays", type=int, default=0, metavar="N",
+                    help="only replay the verify calls (group export) of all layers N times and exit "
+                         "(for HBM byte counters of the verify call)")
     ap.add_argument("--cpu-steps", default="", metavar="WORKLOADS",
                     help="only time the fp64 oracle's steps for these workloads (comma-separated) "
                          "on min(16, host CPUs) threads, and for the 2K and 32K ones also on one "
@@ -276,7 +282,15 @@ def main():
         L = args.layers
     print(f"[bench] {args.workload}: {L} layers, {layer_kv / 1e6:.1f} MB KV per layer, "
           f"export={args.export}, kernel={args.kernel}", file=sys.stderr, flush=True)
-    layers = build_layers(c, L, kernel)
+    layers = build_layers(c, L, kernel, args.export)
+    if args.verify_replays:
+        g_verify = capture(lambda: [lc.verify(export=args.export) for lc in layers])
+        for _ in range(args.verify_replays):
+            g_verify.replay()
+        torch.cuda.synchronize()
+        print(json.dumps({"verify_replays": args.verify_replays, "layers": L, "workload": args.workload,
+                          "algorithmic_bytes_per_launch": ab["verify"]}), flush=True)
+        return
     r = measure(c, layers, args.export, args.steps, args.warmup)
     r["layers"] = L
     fig = workload_figures(c, r, args.export)
@@ -353,7 +367,7 @@ def main():
         for wl in [w for w in args.other_workloads.split(",") if w and w != args.workload]:
             cw = synth.make_case(wl)
             Lw, _ = layer_count(cw, algorithmic_bytes(cw, args.export))
-            lw = build_layers(cw, Lw, kernel)
+            lw = build_layers(cw, Lw, kernel, args.export)
             rw = measure(cw, lw, args.export, min(args.steps, 10), 2)
             rw["layers"] = Lw
             others[wl] = dict(workload_figures(cw, rw, args.export), layers=Lw)
