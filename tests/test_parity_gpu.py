@@ -459,6 +459,15 @@ def _topk_cases():
     s = (np.round(rng.standard_normal((3, mp)) * 64) / 64).astype(np.float32)
     out.append(("moderate_ties", s, np.array([mp, 70_001, 2049], np.int32),
                 np.array([5243, 3500, 2049], np.int32), 5243))
+    # continuous scores with a few exact copies of a value just above the k-th
+    # largest, spread over several chunks: a small tie set at K* of which some
+    # are taken (the resolve's ranked-list path)
+    s = rng.standard_normal((2, mp)).astype(np.float32)
+    P2, k2 = np.array([mp, 100_000], np.int32), np.array([5243, 777], np.int32)
+    for b in range(2):
+        t = np.sort(s[b, :P2[b]])[::-1][k2[b] - 5]
+        s[b, rng.choice(P2[b], 7, replace=False)] = t
+    out.append(("list_ties", s, P2, k2, 5243))
     # continuous scores, ragged lengths around chunk edges, k = 0, k > P, P = 0, P = 1
     s = rng.standard_normal((8, 8192)).astype(np.float32)
     s[6, ::2] = -0.0
