@@ -14,7 +14,9 @@
 //            bin b1 holding it (the sums over chunks of cnt_ge, searched 64
 //            bins at a time: coarse, then the 64-bin window), and K* within
 //            b1 from the candidates (bin b1: staged entries cnt_ge[b1 + 1] ..
-//            cnt_ge[b1] of every chunk) through two 10-bit histograms.  Then
+//            cnt_ge[b1] of every chunk): a histogram of key bits [10, 20)
+//            gives the 22-bit bin b2, then either one wave ranks b2's keys
+//            (when there are at most 64) or a histogram of bits [0, 10) does.  Then
 //            it writes its own chunk's selection: the staged entries above b1,
 //            the candidates above K*, and the keys equal to K* that the tie
 //            rule gives this chunk (lowest positions first, so earlier chunks
@@ -29,11 +31,13 @@
 // entries within a bin, so the result is deterministic although the staging
 // uses LDS atomics.
 //
-// Written around two properties of the hardware: a workgroup barrier waits
-// for every global load and store the wave has in flight, so the stage kernel
-// issues its global writes after its last barrier; and a load whose address
+// Written around three properties of the hardware: a workgroup barrier
+// waits for every global load and store the wave has in flight, so the stage
+// kernel issues its global writes after its last barrier; a load whose address
 // follows a data-dependent branch is not issued together with the others, so
-// each round of loads is computed without branches.
+// each round of loads is computed without branches and with wave-uniform
+// indices; and a register that a load writes cannot be reused before the load
+// returns, so no load writes a half the code never reads.
 #pragma once
 
 #include "select.h"

@@ -27,40 +27,6 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
 // Exponential in base 2 (hardware v_exp_f32).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Device-scope accesses through a buffer resource: the sc1 cache-policy bit
-// gives a store device scope (it is written through to the point where all
-// XCDs' accesses are coherent before its completion is counted) and a load
-// device scope (it reads from that point).  Data that one workgroup hands to
-// another inside a kernel moves this way, so the handoff needs no writeback or
-// invalidation of a whole L2.  Offsets are bytes from the base (below 2^31).
-constexpr int kCachePolicyDevice = 16;    // sc1
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t device_buffer(const void *base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, kBufferWord3);
-}
-__device__ __forceinline__ void store_device(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCachePolicyDevice);
-}
-__device__ __forceinline__ void store_device(__amdgpu_buffer_rsrc_t r, int off, u32x2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCachePolicyDevice);
-}
-__device__ __forceinline__ void store_device(__amdgpu_buffer_rsrc_t r, int off, uint16_t v) {
-  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, kCachePolicyDevice);
-}
-__device__ __forceinline__ u32x4 load_device4(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyDevice);
-}
-__device__ __forceinline__ u32x2 load_device2(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCachePolicyDevice);
-}
-__device__ __forceinline__ uint32_t load_device1(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCachePolicyDevice);
-}
-__device__ __forceinline__ uint16_t load_device_u16(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kCachePolicyDevice);
-}
-
 // Lane 0's value of a float, as a wave-uniform value.  (readfirstlane takes
 // an int: passing the float itself would convert its value, not its bits.)
 __device__ __forceinline__ float first_lane(float x) {
