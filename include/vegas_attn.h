@@ -14,6 +14,14 @@
  *   vg_sparse_draft_attention  attention of draft rows over only the selected
  *                              slots plus the causal tail after the prefix.
  *
+ * Fused forms of the same steps: vg_aggregate_topk_select (aggregation and
+ * top-k in one call) and vg_verify_select (verify with the group export,
+ * aggregation and top-k in one call).  Around the path: the all-rows export
+ * (vg_verify_attention_all_rows), the KV append and prefix bookkeeping
+ * (vg_kv_append, vg_advance_prefix), a query-agnostic selector
+ * (vg_window_select), and a draft call that allocates nothing
+ * (vg_sparse_draft_attention_noalloc).
+ *
  * "Vegas" below is the page "Vegas: Self-Speculative Decoding with
  * Verification-Guided Sparse Attention" (technical summary).
  *
@@ -21,8 +29,9 @@
  * --------------------------------
  * - Every tensor pointer is DEVICE memory owned by the caller.  The library
  *   allocates nothing, keeps no per-call state between calls except inside
- *   the caller's workspace, and never synchronises the stream or copies
- *   device data to the host.  Work is enqueued on `stream` (a hipStream_t
+ *   the caller's workspace (and, for vg_sparse_draft_attention_noalloc only,
+ *   its file-scope scratch array), and never synchronises the stream or
+ *   copies device data to the host.  Work is enqueued on `stream` (a hipStream_t
  *   passed as void*; NULL = the null stream).
  * - Arguments are validated on the host before anything is enqueued.  On any
  *   error nothing is launched and no output is touched.  Values that live on
