@@ -115,7 +115,7 @@ __device__ __forceinline__ int staged_slot(const int *slot_sm, const AttnArgs &a
 template <int D>
 __device__ __forceinline__ void load_tile(KVTile<D> &T, const AttnArgs &a, int b, const SeqList &s,
                                           int e0, int g, int lane, const int *slot_sm, int e_begin,
-                                          int e_end) {
+                                          int e_end, bool pref = false, int pf_slot = 0, int jt = 0) {
   constexpr int DPL = D / 16;
   const int q4 = lane >> 4, i16 = lane & 15;
   const size_t slot_bytes = (size_t)a.num_kv_heads * D * 2;
@@ -124,7 +124,10 @@ __device__ __forceinline__ void load_tile(KVTile<D> &T, const AttnArgs &a, int b
   // Entries past the chunk's end (masked later) reuse its last entry, whose
   // slot is staged.
   const int my_e = min(e0 + (lane & 31), e_end - 1);
-  const int my_slot = staged_slot(slot_sm, a, b, s, e_begin, my_e);
+  // prefetched split: lane l of this wave holds the slot of entry l & 31 of
+  // its tile (l >> 5)
+  const int rs = __shfl(pf_slot, ((my_e - e0) + 32 * jt) & 63);  // (every lane takes part)
+  const int my_slot = pref ? (my_e < s.cnt ? rs : entry_slot(a, b, s, my_e)) : staged_slot(slot_sm, a, b, s, e_begin, my_e);
   const char *kc = static_cast<const char *>(a.k_cache);
   const char *vc = static_cast<const char *>(a.v_cache);
   constexpr int CH = D / 8;       // 16-byte chunks per row
@@ -361,14 +364,17 @@ void attn_mfma_kernel(AttnArgs a_in) {
   const int chunk = a.sparse ? kSparseChunk : kVerifyChunk;
   // Fixed sparse splits (at most kThreads entries, one chunk): this
   // workgroup's part of the explicit slot list is loaded now, together with
-  // the list length rather than after it.  Entries past the selection count
-  // are loaded (they are inside the [B][max_k] list) but never used.
+  // the list length rather than after it, straight into the registers of the
+  // waves that load those entries' K/V rows (no LDS staging, no barrier).
+  // Entries past the selection count are loaded (they are inside the
+  // [B][max_k] list) but never used.
   const bool pref = a.sparse && a.split_tokens > 0 && a.split_tokens <= kThreads;
   int pf_slot = 0;
-  if (pref) {
+  if (pref) {  // lane l of wave v: entry 32 (v + 4 (l >> 5)) + (l & 31) of the split (its tile l >> 5)
     const int seg = blockIdx.x / a.splits;
-    const int e = (blockIdx.x % a.splits) * a.split_tokens + (int)threadIdx.x;
-    if ((int)threadIdx.x < a.split_tokens && e < a.max_k)
+    const int le = 32 * (((int)threadIdx.x >> 6) + kWaves * (((int)threadIdx.x >> 5) & 1)) + ((int)threadIdx.x & 31);
+    const int e = (blockIdx.x % a.splits) * a.split_tokens + le;
+    if (le < a.split_tokens && e < a.max_k)
       pf_slot = a.sel_slot[(size_t)(seg / a.num_kv_heads) * a.max_k + e];
   }
 
@@ -431,13 +437,11 @@ void attn_mfma_kernel(AttnArgs a_in) {
 
     for (int c0 = e_begin; c0 < e_end; c0 += chunk) {
       const int c1 = min(e_end, c0 + chunk);
-      __syncthreads();  // earlier users of slot_sm / the K staging area are done
-      if (pref) {  // the one chunk starts at e_begin = this split's first entry
-        if ((int)threadIdx.x < min(c1, s.cnt) - c0) slot_sm[threadIdx.x] = pf_slot;
-      } else {
+      if (!pref) {  // (a prefetched split is one chunk whose slots are in registers)
+        __syncthreads();  // earlier users of slot_sm / the K staging area are done
         stage_slots(slot_sm, a, b, s, c0, c1);
+        __syncthreads();
       }
-      __syncthreads();
       // This wave's tiles: j = 0 .. nw-1 cover entries c0 + 32 * (wave + 4 j).
       const int ntiles = (c1 - c0 + 31) / 32;
       const int nw = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
@@ -448,20 +452,20 @@ void attn_mfma_kernel(AttnArgs a_in) {
       KVTile<D> T[PF];
 #pragma unroll
       for (int u = 0; u < PF; ++u)
-        if (u < nw) load_tile<D>(T[u], a, b, s, e_of(u), g, lane, slot_sm, c0, c1);
+        if (u < nw) load_tile<D>(T[u], a, b, s, e_of(u), g, lane, slot_sm, c0, c1, pref, pf_slot, u);
       int j = 0;
       for (; j + 2 * PF <= nw; j += PF) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
           compute_tile<D, NT, RAW, SPARSE>(W, T[u], lds.kst[wave], a, b, g, s, e_of(j + u), c1, lane, do_export, vec_export);
-          load_tile<D>(T[u], a, b, s, e_of(j + u + PF), g, lane, slot_sm, c0, c1);
+          load_tile<D>(T[u], a, b, s, e_of(j + u + PF), g, lane, slot_sm, c0, c1, pref, pf_slot, j + u + PF);
         }
       }
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
         if (j + u < nw) {
           compute_tile<D, NT, RAW, SPARSE>(W, T[u], lds.kst[wave], a, b, g, s, e_of(j + u), c1, lane, do_export, vec_export);
-          if (j + u + PF < nw) load_tile<D>(T[u], a, b, s, e_of(j + u + PF), g, lane, slot_sm, c0, c1);
+          if (j + u + PF < nw) load_tile<D>(T[u], a, b, s, e_of(j + u + PF), g, lane, slot_sm, c0, c1, pref, pf_slot, j + u + PF);
         }
       }
 #pragma unroll
