@@ -105,6 +105,20 @@ __device__ __forceinline__ void stage_slots(int *slot_sm, const AttnArgs &a, int
 constexpr int kVerifyChunk = 512 * kPageSize;
 constexpr int kSparseChunk = kSlotSm;
 
+// LDS of the tile loop: the waves' K staging areas and, with GST, the
+// chunk's staged group sums.
+template <int D, bool A16, bool GST>
+struct LoopSmem {
+  KStage<D, A16> kst[kWaves];
+  float gst[kVerifyChunk];
+  __device__ float *staging() { return gst; }
+};
+template <int D, bool A16>
+struct LoopSmem<D, A16, false> {
+  KStage<D, A16> kst[kWaves];
+  __device__ float *staging() { return nullptr; }  // (never dereferenced)
+};
+
 __device__ __forceinline__ int staged_slot(const int *slot_sm, const AttnArgs &a, int b,
                                            const SeqList &s, int e_begin, int e) {
   if (!a.sparse) return slot_sm[(e >> 4) - (e_begin >> 4)] * kPageSize + (e & (kPageSize - 1));
@@ -163,11 +177,13 @@ struct WaveState {
   int xbase[NT];         // 0, or the row r when every row is exported
 };
 
-template <int D, int NT, bool RAW, bool A16>
+// GST: the group sums go to the chunk's LDS staging area `gst` (entry e at
+// gst[e - gc0]) instead of straight to memory.
+template <int D, int NT, bool RAW, bool A16, bool GST>
 __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D> &T,
                                              KStage<D, A16> &ks_sm, const AttnArgs &a, int b, int g,
                                              const SeqList &s, int e0, int e_end, int lane,
-                                             bool do_export, bool vec_export) {
+                                             bool do_export, bool vec_export, float *gst, int gc0) {
   constexpr int KS = D / 32, DPL = D / 16;
   constexpr int CH = D / 8, RPI = 64 / CH, RB = KStage<D, A16>::kRowBytes;
   const int q4 = lane >> 4, i16 = lane & 15;
@@ -246,7 +262,9 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
         for (int c = 0; c < 4; ++c) gs[c] = sum_within_group(gs[c]) * a.scale;
         if (i16 == 0) {
           const int e = e0 + tt * 16 + 4 * q4;
-          if (vec_export && e + 3 < s.p_export) {
+          if (GST) {
+            *reinterpret_cast<f32x4 *>(gst + (e - gc0)) = gs;
+          } else if (vec_export && e + 3 < s.p_export) {
             *reinterpret_cast<f32x4 *>(dst + e) = gs;
           } else {
 #pragma unroll
@@ -346,9 +364,17 @@ void attn_mfma_kernel(AttnArgs a_in) {
   constexpr int KS = D / 32;   // k-steps of the QK^T contraction
   constexpr int DPL = D / 16;  // d values per lane per V row, = number of PV tiles
   constexpr int ROWS = NT * 16;
+  // Group sums staged per chunk (D = 128 verify kernels): a tile's sums go to
+  // LDS, and the whole chunk's range is written at the chunk's end as one
+  // contiguous run with nontemporal stores.  Written straight from each tile
+  // (128 bytes of a row at a time, spread over all workgroups' rows), the
+  // lines reach HBM one by one in the middle of the K/V read stream and cost
+  // far more than their bytes.  The D = 64 kernels, which are sensitive to
+  // any code added to their tile loop, store each tile's sums directly.
+  constexpr bool GST = !SPARSE && D == 128;
   __shared__ union {
-    KStage<D, SPARSE> kst[kWaves];  // during the tile loop
-    MergeSmem<ROWS, D> m;    // after it
+    LoopSmem<D, SPARSE, GST> t;  // during the tile loop
+    MergeSmem<ROWS, D> m;        // after it
   } lds;
   MergeSmem<ROWS, D> &sm = lds.m;
   __shared__ int slot_sm[kSlotSm];
@@ -457,21 +483,35 @@ void attn_mfma_kernel(AttnArgs a_in) {
       for (; j + 2 * PF <= nw; j += PF) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
-          compute_tile<D, NT, RAW, SPARSE>(W, T[u], lds.kst[wave], a, b, g, s, e_of(j + u), c1, lane, do_export, vec_export);
+          compute_tile<D, NT, RAW, SPARSE, GST>(W, T[u], lds.t.kst[wave], a, b, g, s, e_of(j + u), c1, lane, do_export, vec_export, lds.t.staging(), c0);
           load_tile<D>(T[u], a, b, s, e_of(j + u + PF), g, lane, slot_sm, c0, c1, pref, pf_slot, j + u + PF);
         }
       }
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
         if (j + u < nw) {
-          compute_tile<D, NT, RAW, SPARSE>(W, T[u], lds.kst[wave], a, b, g, s, e_of(j + u), c1, lane, do_export, vec_export);
+          compute_tile<D, NT, RAW, SPARSE, GST>(W, T[u], lds.t.kst[wave], a, b, g, s, e_of(j + u), c1, lane, do_export, vec_export, lds.t.staging(), c0);
           if (j + u + PF < nw) load_tile<D>(T[u], a, b, s, e_of(j + u + PF), g, lane, slot_sm, c0, c1, pref, pf_slot, j + u + PF);
         }
       }
 #pragma unroll
       for (int u = 0; u < PF; ++u)
         if (j + PF + u < nw)
-          compute_tile<D, NT, RAW, SPARSE>(W, T[u], lds.kst[wave], a, b, g, s, e_of(j + PF + u), c1, lane, do_export, vec_export);
+          compute_tile<D, NT, RAW, SPARSE, GST>(W, T[u], lds.t.kst[wave], a, b, g, s, e_of(j + PF + u), c1, lane, do_export, vec_export, lds.t.staging(), c0);
+      if (GST && a.group && c0 < s.p_export) {  // the chunk's group sums below the prefix length
+        __syncthreads();
+        const int n = min(c1, s.p_export) - c0;
+        float *dst = a.group + (size_t)(b * a.num_kv_heads + g) * a.max_prefix + c0;
+        for (int i = 4 * (int)threadIdx.x; i < n; i += 4 * kThreads) {
+          const f32x4 v = *reinterpret_cast<const f32x4 *>(lds.t.staging() + i);
+          if (vec_export && i + 3 < n) {
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(dst + i));
+          } else {
+            for (int c = 0; c < 4; ++c)
+              if (i + c < n) dst[i + c] = v[c];
+          }
+        }
+      }
     }
 
     __syncthreads();  // the K staging area becomes the merge area
