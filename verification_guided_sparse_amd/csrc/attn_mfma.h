@@ -105,16 +105,35 @@ __device__ __forceinline__ void stage_slots(int *slot_sm, const AttnArgs &a, int
 constexpr int kVerifyChunk = 512 * kPageSize;
 constexpr int kSparseChunk = kSlotSm;
 
-// LDS of the tile loop: the waves' K staging areas and, with GST, the
-// chunk's staged group sums.
-template <int D, bool A16, bool GST>
+// Raw-logit rows staged per chunk (D = 128 kernels): at most kRawStage
+// logits (rows x positions, 64 KB) plus 4 floats of padding per row (rows 16
+// bytes apart in bank order, so that a tile's 16 rows are written without
+// LDS bank conflicts).  Staging is used when the chunk it allows holds at
+// least kRawStageMin entries (two rows per query head); with more rows
+// (every row exported) the chunks would be so short that restarting the tile
+// pipeline at each one costs more than it saves, and the rows are stored per
+// tile, as in the D = 64 kernels (two workgroups per CU leave no room).
+constexpr int kRawStage = 16384;
+constexpr int kRawStagePad = 4;
+constexpr int kRawStageMin = 1024;
+
+// Chunk length of a verify piece with nx staged raw-logit rows: the largest
+// multiple of the 32-entry tile whose nx rows fit the staging area, at most
+// kVerifyChunk.
+__host__ __device__ constexpr int raw_chunk(int nx) {
+  return ((kRawStage / nx) & ~31) < kVerifyChunk ? ((kRawStage / nx) & ~31) : kVerifyChunk;
+}
+
+// LDS of the tile loop: the waves' K staging areas and NS floats of export
+// staging (the chunk's group sums, then its raw-logit rows).
+template <int D, bool A16, int NS>
 struct LoopSmem {
   KStage<D, A16> kst[kWaves];
-  float gst[kVerifyChunk];
-  __device__ float *staging() { return gst; }
+  float st[NS];
+  __device__ float *staging() { return st; }
 };
 template <int D, bool A16>
-struct LoopSmem<D, A16, false> {
+struct LoopSmem<D, A16, 0> {
   KStage<D, A16> kst[kWaves];
   __device__ float *staging() { return nullptr; }  // (never dereferenced)
 };
@@ -178,16 +197,19 @@ struct WaveState {
 };
 
 // GST: the group sums go to the chunk's LDS staging area `gst` (entry e at
-// gst[e - gc0]) instead of straight to memory.
-template <int D, int NT, bool RAW, bool A16, bool GST>
+// gst[e - gc0]) instead of straight to memory; RAW kernels stage their
+// raw-logit rows likewise in `xst` (row xr = slot * G + head in group, xs
+// floats apart).
+template <int D, int NT, bool RAW, bool A16, bool GST, bool XST>
 __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D> &T,
                                              KStage<D, A16> &ks_sm, const AttnArgs &a, int b, int g,
                                              const SeqList &s, int e0, int e_end, int lane,
-                                             bool do_export, bool vec_export, float *gst, int gc0) {
+                                             bool do_export, bool vec_export, float *gst, int gc0,
+                                             float *xst, int xs) {
   constexpr int KS = D / 32, DPL = D / 16;
   constexpr int CH = D / 8, RPI = 64 / CH, RB = KStage<D, A16>::kRowBytes;
   const int q4 = lane >> 4, i16 = lane & 15;
-  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int Hkv = a.num_kv_heads;
 
   // K rows -> LDS -> operand layout (this wave's staging area only)
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -224,7 +246,8 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
   // Logit export (verify): rows 0 and gamma (or every row), entries below the
   // prefix length.
   if (do_export && e0 < s.p_export) {
-    if (RAW && a.logits) {
+    if (RAW && a.logits) {  // staged (xst set: the chunk's rows are written at its end) or stored here
+      const int Hq = a.num_q_heads;
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) {
         if (W.xrow[rt]) {
@@ -232,18 +255,28 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
             if (W.xrow[rt] & (1 << x)) {
-              const int n_slots = a.export_all ? a.nrows : 2;
-              float *dst = a.logits + ((size_t)(b * n_slots + W.xbase[rt] + x) * Hq + h) * a.max_prefix;
+              const int slot = W.xbase[rt] + x;
+              if (XST && xst) {
+                float *xrow = xst + (slot * a.group_size + (h - g * a.group_size)) * xs;
 #pragma unroll
-              for (int tt = 0; tt < 2; ++tt) {
-                const int e = e0 + tt * 16 + 4 * q4;
-                const f32x4 lv = st[tt][rt] * a.scale;
-                if (vec_export && e + 3 < s.p_export) {
-                  *reinterpret_cast<f32x4 *>(dst + e) = lv;
-                } else {
+                for (int tt = 0; tt < 2; ++tt) {
+                  const int e = e0 + tt * 16 + 4 * q4;
+                  *reinterpret_cast<f32x4 *>(xrow + (e - gc0)) = st[tt][rt] * a.scale;
+                }
+              } else {
+                const int n_slots = a.export_all ? a.nrows : 2;
+                float *dst = a.logits + ((size_t)(b * n_slots + slot) * Hq + h) * a.max_prefix;
 #pragma unroll
-                  for (int c = 0; c < 4; ++c)
-                    if (e + c < s.p_export) dst[e + c] = lv[c];
+                for (int tt = 0; tt < 2; ++tt) {
+                  const int e = e0 + tt * 16 + 4 * q4;
+                  const f32x4 lv = st[tt][rt] * a.scale;
+                  if (vec_export && e + 3 < s.p_export) {
+                    *reinterpret_cast<f32x4 *>(dst + e) = lv;
+                  } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                      if (e + c < s.p_export) dst[e + c] = lv[c];
+                  }
                 }
               }
             }
@@ -364,17 +397,20 @@ void attn_mfma_kernel(AttnArgs a_in) {
   constexpr int KS = D / 32;   // k-steps of the QK^T contraction
   constexpr int DPL = D / 16;  // d values per lane per V row, = number of PV tiles
   constexpr int ROWS = NT * 16;
-  // Group sums staged per chunk (D = 128 verify kernels): a tile's sums go to
-  // LDS, and the whole chunk's range is written at the chunk's end as one
-  // contiguous run with nontemporal stores.  Written straight from each tile
-  // (128 bytes of a row at a time, spread over all workgroups' rows), the
-  // lines reach HBM one by one in the middle of the K/V read stream and cost
-  // far more than their bytes.  The D = 64 kernels, which are sensitive to
-  // any code added to their tile loop, store each tile's sums directly.
+  // Exports staged per chunk (D = 128 verify kernels): a tile's group sums
+  // and raw logits go to LDS, and each of the chunk's rows is written at the
+  // chunk's end as one contiguous run with nontemporal stores.  Written
+  // straight from each tile (128 bytes of a row at a time, spread over all
+  // workgroups' rows), the lines reach HBM one by one in the middle of the
+  // K/V read stream and cost far more than their bytes.  The D = 64 kernels,
+  // which are sensitive to any code added to their tile loop (and run two
+  // workgroups per CU), store each tile's exports directly.
   constexpr bool GST = !SPARSE && D == 128;
+  constexpr bool XST = RAW && !SPARSE && D == 128;
+  constexpr int NS = (GST ? kVerifyChunk : 0) + (XST ? kRawStage + kRawStagePad * kMaxRows : 0);
   __shared__ union {
-    LoopSmem<D, SPARSE, GST> t;  // during the tile loop
-    MergeSmem<ROWS, D> m;        // after it
+    LoopSmem<D, SPARSE, NS> t;  // during the tile loop
+    MergeSmem<ROWS, D> m;       // after it
   } lds;
   MergeSmem<ROWS, D> &sm = lds.m;
   __shared__ int slot_sm[kSlotSm];
@@ -387,7 +423,14 @@ void attn_mfma_kernel(AttnArgs a_in) {
   const int G = a.group_size, M = a.rows, Hq = a.num_q_heads;
   const bool do_export = !a.sparse && (a.logits != nullptr || a.group != nullptr);
   const bool vec_export = (a.max_prefix & 3) == 0;
-  const int chunk = a.sparse ? kSparseChunk : kVerifyChunk;
+  // raw-logit rows of this KV head (two per query head, or every row), and
+  // whether they are staged (then with a shorter chunk and this LDS stride)
+  const int nx = (RAW && a.logits) ? (a.export_all ? a.nrows : 2) * G : 0;
+  const bool xstage = XST && nx > 0 && raw_chunk(nx) >= kRawStageMin;
+  const int chunk = a.sparse ? kSparseChunk : xstage ? raw_chunk(nx) : kVerifyChunk;
+  const int xs = chunk + kRawStagePad;
+  float *const gst = lds.t.staging();
+  float *const xst = lds.t.staging() + (GST ? kVerifyChunk : 0);
   // Fixed sparse splits (at most kThreads entries, one chunk): this
   // workgroup's part of the explicit slot list is loaded now, together with
   // the list length rather than after it, straight into the registers of the
@@ -483,32 +526,45 @@ void attn_mfma_kernel(AttnArgs a_in) {
       for (; j + 2 * PF <= nw; j += PF) {
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
-          compute_tile<D, NT, RAW, SPARSE, GST>(W, T[u], lds.t.kst[wave], a, b, g, s, e_of(j + u), c1, lane, do_export, vec_export, lds.t.staging(), c0);
+          compute_tile<D, NT, RAW, SPARSE, GST, XST>(W, T[u], lds.t.kst[wave], a, b, g, s, e_of(j + u), c1, lane, do_export, vec_export, gst, c0, xstage ? xst : nullptr, xs);
           load_tile<D>(T[u], a, b, s, e_of(j + u + PF), g, lane, slot_sm, c0, c1, pref, pf_slot, j + u + PF);
         }
       }
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
         if (j + u < nw) {
-          compute_tile<D, NT, RAW, SPARSE, GST>(W, T[u], lds.t.kst[wave], a, b, g, s, e_of(j + u), c1, lane, do_export, vec_export, lds.t.staging(), c0);
+          compute_tile<D, NT, RAW, SPARSE, GST, XST>(W, T[u], lds.t.kst[wave], a, b, g, s, e_of(j + u), c1, lane, do_export, vec_export, gst, c0, xstage ? xst : nullptr, xs);
           if (j + u + PF < nw) load_tile<D>(T[u], a, b, s, e_of(j + u + PF), g, lane, slot_sm, c0, c1, pref, pf_slot, j + u + PF);
         }
       }
 #pragma unroll
       for (int u = 0; u < PF; ++u)
         if (j + PF + u < nw)
-          compute_tile<D, NT, RAW, SPARSE, GST>(W, T[u], lds.t.kst[wave], a, b, g, s, e_of(j + PF + u), c1, lane, do_export, vec_export, lds.t.staging(), c0);
-      if (GST && a.group && c0 < s.p_export) {  // the chunk's group sums below the prefix length
+          compute_tile<D, NT, RAW, SPARSE, GST, XST>(W, T[u], lds.t.kst[wave], a, b, g, s, e_of(j + PF + u), c1, lane, do_export, vec_export, gst, c0, xstage ? xst : nullptr, xs);
+      // the chunk's staged exports, entries below the prefix length
+      if ((GST && a.group || xstage) && c0 < s.p_export) {
         __syncthreads();
-        const int n = min(c1, s.p_export) - c0;
-        float *dst = a.group + (size_t)(b * a.num_kv_heads + g) * a.max_prefix + c0;
-        for (int i = 4 * (int)threadIdx.x; i < n; i += 4 * kThreads) {
-          const f32x4 v = *reinterpret_cast<const f32x4 *>(lds.t.staging() + i);
+        const int n = min(c1, s.p_export) - c0, n4 = (n + 3) >> 2;
+        auto put = [&](float *dst, const float *src, int i) {  // entries i .. i+3 of the run
+          const f32x4 v = *reinterpret_cast<const f32x4 *>(src + i);
           if (vec_export && i + 3 < n) {
             __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(dst + i));
           } else {
             for (int c = 0; c < 4; ++c)
               if (i + c < n) dst[i + c] = v[c];
+          }
+        };
+        if (GST && a.group) {
+          float *dst = a.group + (size_t)(b * a.num_kv_heads + g) * a.max_prefix + c0;
+          for (int i = 4 * (int)threadIdx.x; i < n; i += 4 * kThreads) put(dst, gst, i);
+        }
+        if (xstage) {  // row xr = slot * G + head in group
+          const int n_slots = a.export_all ? a.nrows : 2;
+          for (int k = threadIdx.x; k < nx * n4; k += kThreads) {
+            const int xr = k / n4, i = 4 * (k - xr * n4);
+            const int slot = xr / G, h = g * G + (xr - slot * G);
+            float *dst = a.logits + ((size_t)(b * n_slots + slot) * Hq + h) * a.max_prefix + c0;
+            put(dst, xst + xr * xs, i);
           }
         }
       }

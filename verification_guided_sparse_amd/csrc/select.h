@@ -141,54 +141,49 @@ __device__ __forceinline__ void load_bins_desc(const uint32_t *hist, int nbins, 
   for (int i = 0; i < PER; ++i) h[i] = v[(PER - 1 - i) / 4][(PER - 1 - i) % 4];
 }
 
-// Pass 1.  grid (nchunks, B), kP1Threads threads (kP1Per consecutive positions
-// each).  AGG: compute scores from src and write them.  HIST: add the chunk's
-// bits [20,32) histogram to the global one.
-#ifndef VG_P1_THREADS
-#define VG_P1_THREADS 1024
-#endif
-constexpr int kP1Threads = VG_P1_THREADS;
-constexpr int kP1Per = kChunk / kP1Threads;  // 8, 4 or 2
-typedef float p1vec __attribute__((ext_vector_type(kP1Per < 4 ? kP1Per : 4)));
-constexpr int kP1Vec = kP1Per < 4 ? kP1Per : 4;  // floats per load
-constexpr int kP1Loads = kP1Per / kP1Vec;       // loads per row
+// Pass 1.  grid (ceil(max_prefix / kP1Block), B), kP1Threads threads (kP1Per
+// consecutive positions each).  AGG: compute scores from src and write them.
+// HIST: add the block's bits [20,32) histogram to the global one.
+// Aggregation is a latency-bound stream of src rows: the bytes in flight are
+// P x kP1Rows floats whatever the block size, so the rows of a batch are
+// many, and the blocks small enough that every CU has one.
+constexpr int kP1Threads = 256;
+constexpr int kP1Per = 2;
+constexpr int kP1Block = kP1Threads * kP1Per;  // 512 positions
+constexpr int kP1Rows = 32;                    // src rows whose loads are in flight together
+typedef float p1vec __attribute__((ext_vector_type(kP1Per)));
 
 template <bool AGG, bool HIST>
 __global__ __launch_bounds__(kP1Threads) void select_pass1_kernel(SelArgs a) {
   __shared__ uint32_t lh[kBins1];
   const int b = blockIdx.y, w = blockIdx.x, t = threadIdx.x;
   const int P = sel_prefix(a, b);
-  const int nch = (P + kChunk - 1) / kChunk;
-  if (w >= nch) return;
+  if (w >= (P + kP1Block - 1) / kP1Block) return;
   if (HIST) {
     for (int i = t; i < kBins1 / 4; i += kP1Threads) reinterpret_cast<u32x4 *>(lh)[i] = u32x4{0u, 0u, 0u, 0u};
   }
-  const int j0 = w * kChunk + t * kP1Per;
+  const int j0 = w * kP1Block + t * kP1Per;
   float sc[kP1Per];
 #pragma unroll
   for (int i = 0; i < kP1Per; ++i) sc[i] = 0.f;
   if (AGG) {
-    const bool vec = ((a.max_prefix % kP1Vec) == 0) && (j0 + kP1Per <= P);
-    // rows (t, h) of src in order; batches of 8 rows whose loads are in flight together
+    const bool vec = ((a.max_prefix % kP1Per) == 0) && (j0 + kP1Per <= P);
+    // rows (t, h) of src in order, added in that order; batches of kP1Rows
+    // rows whose loads are in flight together
     const int nrow = a.src_rows * a.src_heads;
     const float *base = a.src + (size_t)b * nrow * a.max_prefix;
     if (vec) {
-      constexpr int U = 8;
-      for (int r0 = 0; r0 < nrow; r0 += U) {
-        p1vec v[U][kP1Loads];
+      for (int r0 = 0; r0 < nrow; r0 += kP1Rows) {
+        p1vec v[kP1Rows];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int u = 0; u < kP1Rows; ++u)
+          v[u] = (r0 + u < nrow) ? __builtin_nontemporal_load(reinterpret_cast<const p1vec *>(
+                                       base + (size_t)(r0 + u) * a.max_prefix + j0))
+                                 : p1vec{};
 #pragma unroll
-          for (int q = 0; q < kP1Loads; ++q)
-            v[u][q] = (r0 + u < nrow) ? __builtin_nontemporal_load(reinterpret_cast<const p1vec *>(
-                                            base + (size_t)(r0 + u) * a.max_prefix + j0 + q * kP1Vec))
-                                      : p1vec{};
+        for (int u = 0; u < kP1Rows; ++u)
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-          for (int q = 0; q < kP1Loads; ++q)
-#pragma unroll
-            for (int i = 0; i < kP1Vec; ++i) sc[q * kP1Vec + i] += v[u][q][i];
+          for (int i = 0; i < kP1Per; ++i) sc[i] += v[u][i];
       }
     } else {
       for (int r = 0; r < nrow; ++r) {
@@ -200,13 +195,10 @@ __global__ __launch_bounds__(kP1Threads) void select_pass1_kernel(SelArgs a) {
     }
     float *dst = a.scores_out + (size_t)b * a.max_prefix;
     if (vec) {
+      p1vec o;
 #pragma unroll
-      for (int q = 0; q < kP1Loads; ++q) {
-        p1vec o;
-#pragma unroll
-        for (int i = 0; i < kP1Vec; ++i) o[i] = sc[q * kP1Vec + i];
-        *reinterpret_cast<p1vec *>(dst + j0 + q * kP1Vec) = o;
-      }
+      for (int i = 0; i < kP1Per; ++i) o[i] = sc[i];
+      *reinterpret_cast<p1vec *>(dst + j0) = o;
     } else {
 #pragma unroll
       for (int i = 0; i < kP1Per; ++i)

@@ -469,7 +469,7 @@ vg_status vg_aggregate_scores(int32_t batch, const float *src, int32_t src_rows,
   a.src_rows = src_rows;
   a.src_heads = src_heads;
   if (max_prefix == 0) return VG_OK;
-  const dim3 grid(ceil_div(max_prefix, kChunk), batch);
+  const dim3 grid(ceil_div(max_prefix, kP1Block), batch);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (select_ws) {
     const SelPlan p = plan_select(batch, max_prefix);
@@ -528,8 +528,9 @@ vg_status vg_topk_select(int32_t batch, const float *scores, int32_t max_prefix,
     hipLaunchKernelGGL(select_resolve_kernel, grid, dim3(kResolveThreads), 0, st, a, o);
     return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
   }
+  const dim3 grid1(ceil_div(max_prefix > 0 ? max_prefix : 1, kP1Block), batch);
   if (!(flags & VG_TOPK_PREPASS_DONE))
-    hipLaunchKernelGGL((select_pass1_kernel<false, true>), grid, dim3(kP1Threads), 0, st, a);
+    hipLaunchKernelGGL((select_pass1_kernel<false, true>), grid1, dim3(kP1Threads), 0, st, a);
   hipLaunchKernelGGL(select_pass2_kernel, grid, dim3(kSelThreads), 0, st, a);
   hipLaunchKernelGGL(select_pass3_kernel, grid, dim3(kSelThreads), 0, st, a);
   return hipGetLastError() == hipSuccess ? VG_OK : VG_ERR_HIP;
@@ -576,7 +577,8 @@ vg_status vg_aggregate_topk_select(int32_t batch, const float *src, int32_t src_
     hipLaunchKernelGGL((select_stage_kernel<true>), grid, dim3(kStageThreads), 0, st, a, o);
     hipLaunchKernelGGL(select_resolve_kernel, grid, dim3(kResolveThreads), 0, st, a, o);
   } else {
-    hipLaunchKernelGGL((select_pass1_kernel<true, true>), grid, dim3(kP1Threads), 0, st, a);
+    const dim3 grid1(ceil_div(max_prefix > 0 ? max_prefix : 1, kP1Block), batch);
+    hipLaunchKernelGGL((select_pass1_kernel<true, true>), grid1, dim3(kP1Threads), 0, st, a);
     hipLaunchKernelGGL(select_pass2_kernel, grid, dim3(kSelThreads), 0, st, a);
     hipLaunchKernelGGL(select_pass3_kernel, grid, dim3(kSelThreads), 0, st, a);
   }
