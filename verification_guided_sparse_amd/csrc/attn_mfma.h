@@ -101,8 +101,14 @@ __device__ __forceinline__ void stage_slots(int *slot_sm, const AttnArgs &a, int
 }
 
 // Entries staged per chunk of a piece: verify stages page ids (1 per 16
-// entries), sparse stages slots (1 per entry).
-constexpr int kVerifyChunk = 512 * kPageSize;
+// entries), sparse stages slots (1 per entry).  Each chunk boundary drains
+// the tile pipeline (about 3 us), so the D = 128 verify kernels without the
+// raw export have a long-chunk form (kSlotSm pages, twice the group-sum
+// staging) for calls whose workgroup shares exceed one chunk; it is not the
+// default because the larger LDS allocation costs a short-share call (one
+// chunk per workgroup) about half a microsecond.
+constexpr int kVerifyChunk = kSlotSm / 2 * kPageSize;
+constexpr int kVerifyChunkLong = kSlotSm * kPageSize;
 constexpr int kSparseChunk = kSlotSm;
 
 // Raw-logit rows staged per chunk (D = 128 kernels): at most kRawStage
@@ -389,7 +395,8 @@ __device__ __forceinline__ void compute_tile(WaveState<D, NT> &W, const KVTile<D
 
 // RAW: the raw-logit export is compiled in (verify calls that export raw
 // logits); without it the kernel exports group sums only, or nothing.
-template <int D, int NT, int PF, bool SPARSE, bool RAW = false>
+// LONGC: verify chunks of kVerifyChunkLong entries (D = 128 without RAW).
+template <int D, int NT, int PF, bool SPARSE, bool RAW = false, bool LONGC = false>
 __global__ __launch_bounds__(kThreads, attn_occupancy(D, NT, PF, SPARSE))
 void attn_mfma_kernel(AttnArgs a_in) {
   AttnArgs a = a_in;
@@ -407,7 +414,9 @@ void attn_mfma_kernel(AttnArgs a_in) {
   // workgroups per CU), store each tile's exports directly.
   constexpr bool GST = !SPARSE && D == 128;
   constexpr bool XST = RAW && !SPARSE && D == 128;
-  constexpr int NS = (GST ? kVerifyChunk : 0) + (XST ? kRawStage + kRawStagePad * kMaxRows : 0);
+  static_assert(!LONGC || (D == 128 && !RAW && !SPARSE), "long chunks: D = 128 verify kernels without RAW");
+  constexpr int VCH = LONGC ? kVerifyChunkLong : kVerifyChunk;  // longest verify chunk
+  constexpr int NS = (GST ? VCH : 0) + (XST ? kRawStage + kRawStagePad * kMaxRows : 0);
   __shared__ union {
     LoopSmem<D, SPARSE, NS> t;  // during the tile loop
     MergeSmem<ROWS, D> m;       // after it
@@ -427,10 +436,10 @@ void attn_mfma_kernel(AttnArgs a_in) {
   // whether they are staged (then with a shorter chunk and this LDS stride)
   const int nx = (RAW && a.logits) ? (a.export_all ? a.nrows : 2) * G : 0;
   const bool xstage = XST && nx > 0 && raw_chunk(nx) >= kRawStageMin;
-  const int chunk = a.sparse ? kSparseChunk : xstage ? raw_chunk(nx) : kVerifyChunk;
+  const int chunk = a.sparse ? kSparseChunk : xstage ? raw_chunk(nx) : VCH;
   const int xs = chunk + kRawStagePad;
   float *const gst = lds.t.staging();
-  float *const xst = lds.t.staging() + (GST ? kVerifyChunk : 0);
+  float *const xst = lds.t.staging() + (GST ? VCH : 0);
   // Fixed sparse splits (at most kThreads entries, one chunk): this
   // workgroup's part of the explicit slot list is loaded now, together with
   // the list length rather than after it, straight into the registers of the

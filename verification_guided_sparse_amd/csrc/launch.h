@@ -29,7 +29,8 @@ constexpr int verify_pf(int D, int NT) {
 namespace vg {
 
 // grid = one workgroup per piece of the plan, kThreads threads each
-void launch_mfma128_verify(int nt, const AttnArgs &a, dim3 grid, hipStream_t st);
+// share_entries: the most entries one verify workgroup's share can hold
+void launch_mfma128_verify(int nt, const AttnArgs &a, dim3 grid, hipStream_t st, long long share_entries);
 void launch_mfma128_sparse(int nt, const AttnArgs &a, dim3 grid, hipStream_t st);
 void launch_mfma64_verify(int nt, const AttnArgs &a, dim3 grid, hipStream_t st);
 void launch_mfma64_sparse(int nt, const AttnArgs &a, dim3 grid, hipStream_t st);

@@ -62,6 +62,7 @@ bool use_mfma(const vg_shape *s) {
 // Sparse draft lists are short: fixed splits.
 struct AttnPlan {
   int rows, nt, mr, tile, workgroups, split_tokens, splits;
+  long long share_entries;  // verify: the most entries one workgroup's share can hold
   bool mfma, ok;  // ok: batch and tile counts within the kernels' limits
   size_t off_part_o, off_part_ml, bytes;
 };
@@ -107,6 +108,7 @@ AttnPlan plan_attention(const vg_shape *s, int nrows, long long max_len, bool sp
     const int occ = !p.mfma ? 1 : attn_occupancy(s->head_dim, p.nt, verify_pf(s->head_dim, p.nt), false);
     const int resident = occ * kCUs;
     p.workgroups = (int)std::min<long long>((tiles + kWaves - 1) / kWaves, resident);
+    p.share_entries = (tiles + p.workgroups - 1) / p.workgroups * p.tile;
     p.split_tokens = 0;
     p.splits = 0;
     n_part = p.workgroups + bg;
@@ -159,7 +161,7 @@ vg_status launch_attention(const vg_shape *s, const AttnPlan &p, AttnArgs &a, ch
   if (p.mfma) {
     if (s->head_dim == 128) {
       if (a.sparse) launch_mfma128_sparse(p.nt, a, grid, st);
-      else launch_mfma128_verify(p.nt, a, grid, st);
+      else launch_mfma128_verify(p.nt, a, grid, st, p.share_entries);
     } else {
       if (a.sparse) launch_mfma64_sparse(p.nt, a, grid, st);
       else launch_mfma64_verify(p.nt, a, grid, st);
