@@ -157,7 +157,11 @@ __device__ __forceinline__ void load_tile(KVTile<D> &T, const AttnArgs &a, int b
                                           int e_end, bool pref = false, int pf_slot = 0, int jt = 0) {
   constexpr int DPL = D / 16;
   const int q4 = lane >> 4, i16 = lane & 15;
-  const size_t slot_bytes = (size_t)a.num_kv_heads * D * 2;
+  // A slot is a row index of the cache (non-negative, below 2^31) and a row
+  // is at most a few KB, so a row's byte offset is one 32 x 32 -> 64-bit
+  // multiply-add (a 64-bit product would take three quarter-rate multiplies
+  // per load address).
+  const uint32_t slot_bytes = (uint32_t)a.num_kv_heads * D * 2;
   const size_t head_off = (size_t)g * D * 2;
   // slot of entry e0 + (lane & 31); each lane then picks the slots it loads.
   // Entries past the chunk's end (masked later) reuse its last entry, whose
@@ -175,13 +179,13 @@ __device__ __forceinline__ void load_tile(KVTile<D> &T, const AttnArgs &a, int b
   for (int i = 0; i < D / 16; ++i) {
     const int row = i * RPI + lane / CH;
     const int ks_slot = __shfl(my_slot, row);
-    const char *krow = kc + (size_t)ks_slot * slot_bytes + head_off + (lane % CH) * 16;
+    const char *krow = kc + (uint64_t)(uint32_t)ks_slot * slot_bytes + head_off + (lane % CH) * 16;
     T.kraw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(krow));
   }
 #pragma unroll
   for (int v = 0; v < 8; ++v) {
     const int vs = __shfl(my_slot, v < 4 ? 4 * q4 + v : 12 + 4 * q4 + v);
-    const char *vrow = vc + (size_t)vs * slot_bytes + head_off + i16 * (DPL * 2);
+    const char *vrow = vc + (uint64_t)(uint32_t)vs * slot_bytes + head_off + i16 * (DPL * 2);
     if constexpr (D == 128)
       T.vr[v].w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vrow));
     else
