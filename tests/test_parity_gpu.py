@@ -172,6 +172,9 @@ SMALL = {
     # one query head per KV head: plain decode attention
     "g1_decode": lambda: synth.small("c5_gptoss_64k", prefix=(3000, 700), num_q_heads=8, num_kv_heads=8,
                                      gamma=2),
+    # the same at D = 128: two staged raw rows per KV head (8192-entry chunks)
+    "g1_d128": lambda: synth.small("c2_qwen3_32k", prefix=(3000, 700), num_q_heads=8, num_kv_heads=8,
+                                   gamma=2),
     # 64 ragged sequences under a permuted pool: many work-split segments
     "many_seqs": lambda: synth.small("c2_qwen3_32k", prefix=tuple(17 + (i * 613) % 1900 for i in range(64)),
                                      gamma=3, paging="permuted", ramp=0, spans=0),
