@@ -49,6 +49,13 @@
  *   A slot id is the index of a page of one token (Vegas section 3, sparse
  *   execution: selected token indices are passed as page indices of a
  *   page-size-1 PagedAttention call).
+ *   Placement (performance only; any 16-byte aligned bases work): give the V
+ *   cache a base 256 bytes past the alignment of the K cache's base (for
+ *   example both from 2 MB-aligned allocations, V starting 256 bytes in).
+ *   The kernels read the K and V rows of a head together; with equally
+ *   aligned bases those rows have the same low address bits and load the
+ *   same HBM channels.  Measured on MI355X: the 128K verify call without
+ *   export 97 -> 93.5 us, the batch-8 ragged one 404 -> 383 us.
  * - Query head h uses KV head h / (Hq / Hkv).
  * - Outputs are fp32.
  */

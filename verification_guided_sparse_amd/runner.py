@@ -19,6 +19,20 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
+# The V cache starts this many bytes into its own allocation, so that it sits
+# 256 bytes past the K cache's (2 MB) alignment: same-head K and V rows then
+# fall on different HBM channels (the cache placement note in vegas_attn.h).
+V_CACHE_OFFSET = 256
+
+
+def _v_cache(t: torch.Tensor) -> torch.Tensor:
+    """A copy of the V cache t that starts V_CACHE_OFFSET bytes into its allocation."""
+    buf = torch.empty(t.numel() * t.element_size() + V_CACHE_OFFSET, dtype=torch.uint8, device=t.device)
+    v = buf[V_CACHE_OFFSET:].view(t.dtype).view(t.shape)
+    v.copy_(t)
+    return v
+
+
 class DeviceCase:
     """One workload resident on the GPU, with every buffer the path writes."""
 
@@ -44,15 +58,16 @@ class DeviceCase:
             self.q = _dev(c.q, dev)
             self.q_draft = _dev(c.q_draft, dev)  # [gamma][B][Hq][D]
             self.k_cache = _dev(c.k_cache, dev)
-            self.v_cache = _dev(c.v_cache, dev)
+            self.v_cache = _v_cache(_dev(c.v_cache, dev))
             pt = np.full((c.batch, self.max_pages), -1, dtype=np.int32)
             pt[:, : c.max_pages] = c.page_table
             self.page_table = _dev(pt, dev)
             self.prefix_len = _dev(c.prefix_len, dev)
             self.k = _dev(c.k, dev)
         else:
-            for n in ("q", "q_draft", "k_cache", "v_cache", "page_table", "prefix_len"):
+            for n in ("q", "q_draft", "k_cache", "page_table", "prefix_len"):
                 setattr(self, n, getattr(like, n).clone())
+            self.v_cache = _v_cache(like.v_cache)
             self.k = _dev(c.k, dev)  # the budget may differ (same inputs, another k)
         f32 = dict(dtype=torch.float32, device=dev)
         i32 = dict(dtype=torch.int32, device=dev)
