@@ -408,15 +408,15 @@ void attn_mfma_kernel(AttnArgs a_in) {
   constexpr int KS = D / 32;   // k-steps of the QK^T contraction
   constexpr int DPL = D / 16;  // d values per lane per V row, = number of PV tiles
   constexpr int ROWS = NT * 16;
-  // Exports staged per chunk (D = 128 verify kernels): a tile's group sums
-  // and raw logits go to LDS, and each of the chunk's rows is written at the
-  // chunk's end as one contiguous run with nontemporal stores.  Written
+  // Exports staged per chunk (verify kernels): a tile's group sums and (at
+  // D = 128) raw logits go to LDS, and each of the chunk's rows is written at
+  // the chunk's end as one contiguous run with nontemporal stores.  Written
   // straight from each tile (128 bytes of a row at a time, spread over all
   // workgroups' rows), the lines reach HBM one by one in the middle of the
-  // K/V read stream and cost far more than their bytes.  The D = 64 kernels,
-  // which are sensitive to any code added to their tile loop (and run two
-  // workgroups per CU), store each tile's exports directly.
-  constexpr bool GST = !SPARSE && D == 128;
+  // K/V read stream and cost far more than their bytes.  The D = 64 kernels
+  // run two workgroups per CU and leave no LDS for raw rows, which they
+  // store per tile.
+  constexpr bool GST = !SPARSE;
   constexpr bool XST = RAW && !SPARSE && D == 128;
   static_assert(!LONGC || (D == 128 && !RAW && !SPARSE), "long chunks: D = 128 verify kernels without RAW");
   constexpr int VCH = LONGC ? kVerifyChunkLong : kVerifyChunk;  // longest verify chunk
