@@ -32,6 +32,9 @@
 //    `at` holds d = DPL*i16 + at for the 8 tokens.
 //  * tok(q4, v) = v < 4 ? 4*q4 + v : 16 + 4*q4 + (v - 4) is exactly the token
 //    set lane (q4, i16) holds in the S^T result, so P^T needs no lane movement.
+//  * Exports (verify): a tile's group sums, and at D = 128 its raw logits, go
+//    to an LDS staging area and leave as contiguous nontemporal runs at the
+//    end of each chunk of the piece (see the kernel).
 #pragma once
 
 #include "attn_common.h"
