@@ -621,19 +621,26 @@ def test_max_batch_parity(torch_cuda):
 
 
 @pytest.mark.parametrize("pad", [1, 64])
-@pytest.mark.parametrize("export,prefix", [("both", (100003, 61441)), ("group", (131071, 130001, 129007, 131000, 120007))])
-def test_staged_exports_multichunk(torch_cuda, pad, export, prefix):
-    """Exports staged in LDS over several chunks of one workgroup's piece
-    (D = 128), ragged lists whose pieces straddle (sequence, KV head) lists,
-    and export rows whose stride is not a multiple of 4 floats (pad=1: the
-    runs' scalar tails).  Raw and group export: 2048-entry chunks for the raw
-    rows.  Group export alone over five long sequences: about 20K entries per
-    workgroup, so the long-chunk kernel runs over two 16384-entry chunks.  Entries
-    past each sequence's prefix length stay as they were (zero)."""
+@pytest.mark.parametrize("wl,export,prefix", [
+    ("c3_qwen3_128k", "both", (100003, 0, 61441)),
+    ("c3_qwen3_128k", "group", (131071, 130001, 129007, 131000, 120007)),
+    ("c5_gptoss_64k", "both", (131071, 130001, 129007, 120007, 131000)),
+])
+def test_staged_exports_multichunk(torch_cuda, pad, wl, export, prefix):
+    """Exports staged in LDS over several chunks of one workgroup's piece,
+    ragged lists whose pieces straddle (sequence, KV head) lists, and export
+    rows whose stride is not a multiple of 4 floats (pad=1: the runs' scalar
+    tails).  D = 128, raw and group export: 2048-entry chunks for the raw rows,
+    and an empty sequence between two long ones.  D = 128, group export alone
+    over five long sequences: about 20K entries per workgroup, so the
+    long-chunk kernel runs over two 16384-entry chunks.  D = 64 (two
+    workgroups per CU, raw rows stored per tile): about 10K entries per
+    workgroup, two 8192-entry chunks of staged group sums.  Entries past each
+    sequence's prefix length stay as they were (zero)."""
     from verification_guided_sparse_amd.runner import DeviceCase
     torch = torch_cuda
-    c = synth.make_case(synth.small("c3_qwen3_128k", prefix=prefix, k_pct=2))
-    _say(f"[parity] staged exports {export} P={list(c.prefix_len)} pad={pad}")
+    c = synth.make_case(synth.small(wl, prefix=prefix, k_pct=2))
+    _say(f"[parity] staged exports {wl} {export} P={list(c.prefix_len)} pad={pad}")
     dc = DeviceCase(c, pad=pad)
     out_ref, logits_ref, group_ref = _oracle_all(c)
     dc.verify(export=export)
