@@ -2,14 +2,14 @@
 //
 // Scores map to order-preserving 32-bit keys (larger score <-> larger key;
 // -0.0 is folded onto +0.0).  The k-th largest key K* is found by a radix
-// select over key bits [20,32) / [10,20) / [0,10), every pass spread over
-// chunks of 2048 positions:
+// select over key bits [20,32) / [10,20) / [0,10), passes 2 and 3 spread
+// over chunks of 2048 positions:
 //
-//   pass 1  (one workgroup per chunk) LDS histogram of bits [20,32), merged
-//           into the sequence's global histogram with atomics (optionally
-//           fused with the aggregation that produces the scores).  Also clears
-//           the bits [10,20) histogram pass 2 fills.  (More workgroups per
-//           chunk make the atomics on the busiest bins contend.)
+//   pass 1  (one workgroup per 512 positions) LDS histogram of bits [20,32),
+//           merged into the sequence's global histogram with atomics
+//           (optionally fused with the aggregation that produces the scores,
+//           a latency-bound stream of the export that wants many workgroups).
+//           Also clears the bits [10,20) histogram pass 2 fills.
 //   pass 2  (one workgroup per chunk) finds the bin b1 holding K*, counts the
 //           chunk's entries above b1, stages its candidates (bin == b1) in
 //           position order and adds their bits [10,20) to a second global
