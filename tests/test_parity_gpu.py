@@ -657,6 +657,46 @@ def test_staged_exports_multichunk(torch_cuda, pad, wl, export, prefix):
         assert not group[b, :, P:].any(), f"group export written past the prefix of sequence {b}"
 
 
+@pytest.mark.parametrize("name,export", [("c2_small", "both"), ("c5_small", "group"), ("c4_small", "raw")])
+def test_cache_bases_at_any_16_byte_offset(torch_cuda, name, export):
+    """The kernels take any 16-byte-aligned K and V cache bases (the placement
+    the runner uses only speeds them up): with the caches moved to other
+    offsets into their allocations, a whole iteration (verify with its
+    exports, aggregation, top-k, every draft step) gives bit-identical
+    results."""
+    import torch
+    from verification_guided_sparse_amd.runner import DeviceCase
+    c = synth.make_case(SMALL[name]())
+    _say(f"[parity] cache base offsets {name} export={export}")
+    dc = DeviceCase(c)
+    names = ["out", "scores", "sel_pos", "sel_slot", "sel_count", "draft_out"]
+    names += {"both": ["logits", "group"], "group": ["group"], "raw": ["logits"]}[export]
+
+    def run():
+        if export == "both":
+            dc.verify(export="both")
+            dc.select(src="group")
+            for s in range(c.gamma):
+                dc.sparse(step=s)
+        else:
+            dc.iteration(export=export)
+        torch.cuda.synchronize()
+        return {n: dc.host(n).copy() for n in names}
+
+    def rebase(t, off):  # a copy of t starting `off` bytes into a fresh allocation
+        buf = torch.empty(t.numel() * t.element_size() + off, dtype=torch.uint8, device=t.device)
+        v = buf[off:].view(t.dtype).view(t.shape)
+        v.copy_(t)
+        return v
+
+    ref = run()
+    for k_off, v_off in ((16, 48), (4112, 0), (0, 0)):
+        dc.k_cache, dc.v_cache = rebase(dc.k_cache, k_off), rebase(dc.v_cache, v_off)
+        got = run()
+        for n in names:
+            assert np.array_equal(got[n], ref[n]), f"{n} differs with K at +{k_off}, V at +{v_off}"
+
+
 # ------------------------------------------------------------------ full sizes
 
 @pytest.mark.parametrize("name", ["c1_tiny", "c2_qwen3_32k", "c3_qwen3_128k", "c5_gptoss_64k", "c4_ragged_b8"])
