@@ -269,6 +269,7 @@ def main():
     import torch
     from verification_guided_sparse_amd import _binding as vg
     from verification_guided_sparse_amd import synth
+    from verification_guided_sparse_amd.runner import V_CACHE_OFFSET
 
     vg.lib()  # fail loudly if the HIP library is missing
     if args.sweep:
@@ -325,6 +326,7 @@ def main():
             "layers_per_step": L,
             "export": args.export,
             "kernel": args.kernel,
+            "v_cache_offset_bytes": V_CACHE_OFFSET,
             "parallelism": "single-gpu",
         },
         "step_ms": {"median": round(r["step_ms_median"], 4), "p10": round(r["step_ms_p10"], 4),
